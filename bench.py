@@ -1,0 +1,225 @@
+"""Benchmark: denoising steps/s and tokens/s of the SureLock step engine at the
+LLaDA-8B shape (32 layers, d=4096, 32x128 MHA, SwiGLU 12288, vocab 126464,
+bf16), one sequence of N=512 (128 random prompt tokens + 384 masked), on one
+GPU, with synthetic random-init weights.
+
+A "step" is one denoising iteration of the whole hot path: dlm_step (active
+set compaction, per-layer projections / rotary / K-V scatter / attention over
+all cached positions / FFN on the active rows, LM head, vocabulary
+statistics) + dlm_lock_update (top-k unmasking and the lock test).  The timed
+steps follow a decoding run from its first step (a new run starts every
+128 steps).  `value` is the configured lock setting (KL <= 1e-3, max-prob >=
+0.9, 2 consecutive steps); the scheduled-lock and vanilla (no locking) runs
+are reported alongside.
+
+Per-kernel times come from HIP events recorded on the engine's stream in a
+second pass over the same steps; the roofline entry is for the kernel class
+with the largest share of that time.  The CPU baseline times the oracle on a
+bounded sample (see cpu_baseline.sample).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "denoising steps/s + tokens/s, LLaDA-8B shape N=512, 1 GPU; MFMA% / HBM%"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def run_steps(eng_factory, K, timing=False):
+    """K steps from the start of a run (new run every `steps` steps).
+    Returns (seconds, decoded tokens, list of M, engine-timing dict or None)."""
+    import torch
+    import oracle
+    acc = {}
+
+    def absorb(e):
+        for k, v in e.read_timing().items():
+            a = acc.setdefault(k, dict(ms=0.0, launches=0, bytes=0.0, flops=0.0))
+            for f in a:
+                a[f] += v[f]
+
+    eng = eng_factory()
+    if timing:
+        eng.set_timing(True)
+    run = eng.run
+    ms, toks = [], 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if eng.t >= run.steps:
+            if timing:
+                absorb(eng)
+            eng.close()
+            eng = eng_factory()
+            if timing:
+                eng.set_timing(True)
+        ms.append(eng.step())
+        eng.lock_update()
+        toks += oracle.unit_schedule(run, eng.t - 1)["k"] * run.batch
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    if timing:
+        absorb(eng)
+    eng.close()
+    return dt, toks, ms, (acc if timing else None)
+
+
+def roofline_entry(tim, setting_ms):
+    # dominant class by total event time
+    name = max(tim, key=lambda k: tim[k]["ms"])
+    t = tim[name]
+    avg_s = t["ms"] / 1e3 / max(t["launches"], 1)
+    flops = t["flops"] / max(t["launches"], 1)
+    byts = t["bytes"] / max(t["launches"], 1)
+    mean_m = sum(setting_ms) / len(setting_ms)
+    if flops > 0 and flops / max(byts, 1.0) >= RIDGE:
+        ach = flops / avg_s / 1e12
+        return name, dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS,
+                          unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
+                          kernel=name, avg_launch_us=round(avg_s * 1e6, 2),
+                          flops_per_launch=flops, bytes_per_launch=byts,
+                          launches=t["launches"], mean_active_rows=round(mean_m, 1))
+    ach = byts / avg_s / 1e9
+    return name, dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                      frac=round(ach / PEAK_HBM_GBS, 4), traffic=None, kernel=name,
+                      avg_launch_us=round(avg_s * 1e6, 2), flops_per_launch=flops,
+                      bytes_per_launch=byts, launches=t["launches"],
+                      mean_active_rows=round(mean_m, 1))
+
+
+def cpu_baseline(shape, run):
+    """Oracle on a bounded sample: one full-width layer at step 0 (M = 512
+    active rows, attention over N = 512) plus the LM head and statistics for
+    8 sampled rows, extrapolated to one configured-setting step (M = 384,
+    32 layers, LM head on 384 rows)."""
+    import dataclasses
+    import numpy as np
+    import oracle
+    import synth
+    one = dataclasses.replace(shape, n_layers=1)
+    W = synth.gen_weights(one)
+    pr = synth.gen_prompts(one, run)
+    o = oracle.Oracle(one, W, run, synth.LOCK_SETTINGS["natural"], pr)
+    t0 = time.perf_counter()
+    o.step(sample_rows=list(range(8)))
+    t_all = time.perf_counter() - t0
+    # split the sample's time into its layer part and LM-head part by FLOPs
+    d, V, N = one.d_model, one.vocab, run.seq_len
+    f_layer = oracle.closed_form_flops(one, [N], N) - 2.0 * N * d * V
+    f_head8 = 2.0 * 8 * d * V
+    rate = (f_layer + f_head8) / t_all  # FLOP/s of the oracle on this sample
+    M = run.seq_len - run.prompt_len
+    f_step = oracle.closed_form_flops(shape, [M], N)
+    step_s = f_step / rate
+    return dict(value=round(1.0 / step_s, 6), unit="steps/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=(f"oracle (C++ fp64, OpenMP) on 1 of 32 layers at full width for all 512 "
+                        f"rows of step 0 plus the LM head for 8 rows: {t_all:.1f} s, "
+                        f"{rate / 1e9:.1f} GFLOP/s; extrapolated by closed-form FLOPs to a "
+                        f"384-row, 32-layer step ({f_step / 1e12:.2f} TFLOP)"),
+                sample_seconds=round(t_all, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-settings", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the step engine has no multi-GPU path "
+              "(data parallelism over sequences would need no per-step exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from selective_token_recompute_amd import engine as E
+
+    shape, run = synth.CONFIGS["llada8b"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating random-init weights on the device ...")
+    dw = E.random_device_weights(shape, seed=0, device=dev)
+    prompts = torch.from_numpy(synth.gen_prompts(shape, run)).to(dev)
+
+    def factory(setting):
+        return lambda: E.Engine(shape, dw, run, synth.LOCK_SETTINGS[setting], prompts)
+
+    K, Wm = args.steps, args.warmup
+    results = {}
+    settings = ["natural"] + ([] if args.no_extra_settings else ["scheduled", "vanilla"])
+    for s in settings:
+        if Wm > 0:
+            run_steps(factory(s), Wm)
+        dt, toks, ms, _ = run_steps(factory(s), K)
+        log(f"[{s}] {K} steps in {dt * 1e3:.1f} ms -> {K / dt:.1f} steps/s, "
+            f"{toks / dt:.1f} tokens/s, mean M {sum(ms) / len(ms):.1f}")
+        results[s] = dict(seconds=dt, tokens=toks, ms=ms)
+
+    # per-kernel event timing over the same steps (configured setting)
+    _, _, ms_nat, tim = run_steps(factory("natural"), K, timing=True)
+    dom, roof = roofline_entry(tim, ms_nat)
+    kernels = {k: dict(ms_total=round(v["ms"], 3), launches=v["launches"],
+                       us_avg=round(v["ms"] * 1e3 / max(v["launches"], 1), 2))
+               for k, v in tim.items() if v["launches"]}
+    for k, v in tim.items():
+        if v["launches"] and v["ms"] > 0:
+            avg = v["ms"] / 1e3 / v["launches"]
+            if v["flops"] > 0:
+                kernels[k]["tflops"] = round(v["flops"] / v["launches"] / avg / 1e12, 1)
+            if v["bytes"] > 0:
+                kernels[k]["gbs"] = round(v["bytes"] / v["launches"] / avg / 1e9, 1)
+    log(f"dominant kernel: {dom} {roof}")
+
+    nat = results["natural"]
+    out = {
+        "metric": METRIC,
+        "value": round(K / nat["seconds"], 3),
+        "unit": "steps/s",
+        "tokens_per_s": round(nat["tokens"] / nat["seconds"], 2),
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(nat["seconds"] * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (random-init weights N(0,0.02), random prompts)",
+        "config": {"workload": "LLaDA-8B-shaped denoising step, B=1, N=512 (128 prompt + 384 "
+                               "masked), 128-step runs, lock: KL<=1e-3 & max-prob>=0.9 x2",
+                   "global_batch": run.batch, "seq_len": run.seq_len, "parallelism": "none"},
+        "mean_active_rows": round(sum(nat["ms"]) / len(nat["ms"]), 1),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    for s in settings[1:]:
+        r = results[s]
+        out[f"{s}_lock"] = dict(steps_per_s=round(K / r["seconds"], 3),
+                                tokens_per_s=round(r["tokens"] / r["seconds"], 2),
+                                mean_active_rows=round(sum(r["ms"]) / len(r["ms"]), 1))
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(shape, run)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

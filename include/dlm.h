@@ -1,0 +1,190 @@
+/*
+ * dlm.h -- C ABI of the MI355X (gfx950) denoising-step engine for masked
+ * diffusion language models with converged-token locking.
+ *
+ * Method: SureLock, as explained on the page "Stopping Computation for
+ * Converged Tokens in Masked Diffusion-LM Decoding" (gist.science explainer,
+ * §1 Problem statement, §2 Methodology).  A denoising iteration recomputes
+ * only the M positions that are still active; locked positions keep their
+ * per-layer K and V in a cache that every active query still attends to, so
+ * the per-step cost is O(M N d) + O(M d^2) instead of O(N^2 d).  Positions
+ * are unmasked by confidence-ranked top-k inside semi-autoregressive blocks
+ * (page "Accelerating Diffusion LLMs with SlowFast Sampling", §1 and §2).
+ *
+ * Conventions
+ *  - Every call returns an int status: DLM_OK or a negative DLM_E_* code.
+ *    No call throws, exits or prints.
+ *  - Argument errors are detected on the host before any launch and leave
+ *    the state untouched.
+ *  - Device-side numeric errors (a non-finite log-normaliser) are latched in
+ *    a device word and reported as DLM_E_NUMERIC by the next dlm_step.
+ *  - All launches go on the stream given to dlm_step_init.  Calls are
+ *    asynchronous except where stated.  A handle is driven by one thread.
+ *  - The library never allocates device memory.  Weights and prompts are
+ *    caller-owned device memory, borrowed (not copied) and must outlive the
+ *    handle.  All mutable state lives in the caller's state_mem block of
+ *    dlm_state_bytes() bytes (256-byte aligned).
+ *  - Linear maps y = x W^T store W as [out_features][in_features], row-major
+ *    and contiguous.  Element type is float (DLM_FP32) or bfloat16 stored as
+ *    uint16 (DLM_BF16) for every weight, norm gain and the embedding.
+ */
+#ifndef DLM_H
+#define DLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DLM_OK = 0,
+  DLM_E_INVALID = -1,     /* bad argument or descriptor */
+  DLM_E_SIZE = -2,        /* state_mem too small */
+  DLM_E_HIP = -3,         /* a HIP runtime call failed */
+  DLM_E_STATE = -4,       /* call out of order (step twice, update before step, t >= steps) */
+  DLM_E_UNSUPPORTED = -5, /* shape outside what the kernels support */
+  DLM_E_NUMERIC = -6      /* device latched a non-finite posterior */
+};
+
+enum { DLM_FP32 = 0, DLM_BF16 = 1 };
+enum { DLM_LOCK_NONE = 0, DLM_LOCK_TEST = 1 };
+
+/* Model shape.  Pre-RMSNorm bidirectional transformer, SwiGLU FFN, untied LM
+ * head, no biases, rotary embedding with half-split pairs (component j with
+ * j + head_dim/2, angle pos * rope_base^(-2j/head_dim)).  Query head h reads
+ * K/V head h * n_kv_heads / n_heads.  The mask token's logit is forced to
+ * -inf, so it is never decoded.  Requires n_heads % n_kv_heads == 0, even
+ * head_dim <= 256, 0 <= mask_id < vocab. */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ff, vocab, mask_id;
+  float rope_base; /* <= 0: no rotary embedding */
+  float rms_eps;
+  int32_t dtype;   /* DLM_FP32 | DLM_BF16 */
+} dlm_model_desc;
+
+/* Device pointers, element type per dlm_model_desc.dtype.  Per-layer arrays
+ * are host arrays of n_layers device pointers (read during dlm_step_init and
+ * copied into the handle). */
+typedef struct {
+  const void* tok_emb;           /* [vocab][d_model] */
+  const void* final_norm;        /* [d_model] */
+  const void* lm_head;           /* [vocab][d_model] */
+  const void* const* attn_norm;  /* L x [d_model] */
+  const void* const* w_qkv;      /* L x [(n_heads + 2 n_kv_heads) head_dim][d_model]: q heads, k heads, v heads */
+  const void* const* w_o;        /* L x [d_model][n_heads head_dim] */
+  const void* const* ffn_norm;   /* L x [d_model] */
+  const void* const* w_gate;     /* L x [d_ff][d_model] */
+  const void* const* w_up;       /* L x [d_ff][d_model] */
+  const void* const* w_down;     /* L x [d_model][d_ff] */
+} dlm_weights;
+
+/* One decoding run.  Positions [0, prompt_len) hold the prompt, the rest
+ * start as mask_id.  The generated span is split into blocks of block_len;
+ * the steps are split over the blocks as T_b = floor(T(b+1)/n_blk) -
+ * floor(T b/n_blk), and the s-th step of block b unmasks
+ * floor(G_b(s+1)/T_b) - floor(G_b s/T_b) positions (requires steps >= n_blk).
+ * Lock test (policy DLM_LOCK_TEST), for every active position whose input
+ * token this step was real: pass = KL defined && KL <= kl_eps && conf >=
+ * conf_tau; a counter of consecutive passes locks the position at n_consec.
+ * KL is KL(p_t || p_{t-1}) (kl_dir 0) or KL(p_{t-1} || p_t) (kl_dir 1).  With
+ * lock_prompt_after_first_step, every prompt position locks after step 0. */
+typedef struct {
+  int32_t batch, seq_len, prompt_len, steps, block_len;
+  float kl_eps, conf_tau;
+  int32_t n_consec, kl_dir, lock_prompt_after_first_step, lock_policy;
+} dlm_run_desc;
+
+/* Replay override for dlm_lock_update (host pointers).  n_commit >= 0 replaces
+ * the top-k choice by the listed (seq, pos, tok) commits; lock_bits non-null
+ * replaces the lock test: bits |= lock_bits ([batch][ceil(seq_len/64)]) and
+ * the counters are set from counters ([batch][seq_len]) when non-null, else
+ * kept. */
+typedef struct {
+  const int32_t* commit_seq;
+  const int32_t* commit_pos;
+  const int32_t* commit_tok;
+  int32_t n_commit; /* < 0: no commit override */
+  const uint64_t* lock_bits;
+  const int32_t* counters;
+} dlm_override;
+
+typedef struct dlm_handle dlm_handle;
+
+/* Bytes of state_mem needed for this model and run; 0 if the descriptors are
+ * invalid. */
+size_t dlm_state_bytes(const dlm_model_desc* model, const dlm_run_desc* run);
+
+/* Validates the descriptors, carves state_mem, zeroes the lock bits, counters
+ * and flags, writes tokens (prompt then mask_id) and builds the rotary table.
+ * prompt_tokens: device int32 [batch][prompt_len].  hip_stream: a hipStream_t
+ * (NULL: the default stream).  Enqueued on the stream; *out receives a
+ * host-allocated handle freed by dlm_destroy. */
+int dlm_step_init(const dlm_model_desc* model, const dlm_weights* weights,
+                  const dlm_run_desc* run, const int32_t* prompt_tokens, void* state_mem,
+                  size_t state_bytes, void* hip_stream, dlm_handle** out);
+
+/* One denoising iteration over the active positions: compaction of the
+ * active set from the lock bitmask, then per layer RMSNorm, QKV projection,
+ * rotary embedding and K/V scatter into the cache, attention of the active
+ * queries over all seq_len cached positions, out-projection, SwiGLU FFN; then
+ * final norm, LM head and the vocabulary statistics (log-normaliser, argmax,
+ * max-probability confidence, KL against the previous step's posterior).
+ * Synchronises the stream once (to read the active count).  *m_tot_out (if
+ * non-null) receives the number of active rows.  DLM_E_STATE if a step is
+ * pending its dlm_lock_update or all steps were taken. */
+int dlm_step(dlm_handle* h, int32_t* m_tot_out);
+
+/* State transition after dlm_step: commit (unmask) the top-k, then the lock
+ * test and the monotone bitmask update; ov (nullable) replays given
+ * decisions.  Asynchronous except for the copy of override arrays. */
+int dlm_lock_update(dlm_handle* h, const dlm_override* ov);
+
+/* Device pointer and element count of a state array (aliases state_mem;
+ * valid until the next dlm_step or dlm_lock_update). */
+enum {
+  DLM_GET_TOKENS = 0,    /* int32  [batch][seq_len] */
+  DLM_GET_LOCK_BITS = 1, /* uint64 [batch][ceil(seq_len/64)] */
+  DLM_GET_COUNTERS = 2,  /* int32  [batch][seq_len] */
+  DLM_GET_ROW_SEQ = 3,   /* int32  [M] sequence of each active row (this step) */
+  DLM_GET_ROW_POS = 4,   /* int32  [M] position of each active row */
+  DLM_GET_ARGMAX = 5,    /* int32  [M] */
+  DLM_GET_CONF = 6,      /* float  [M] */
+  DLM_GET_KL = 7,        /* float  [M] (NaN where undefined) */
+  DLM_GET_HAS_KL = 8,    /* int32  [M] */
+  DLM_GET_LSE = 9,       /* float  [M] */
+  DLM_GET_LOGITS = 10,   /* float  [batch][seq_len][vocab]; rows of this step's active positions */
+  DLM_GET_ROW_REAL = 11, /* int32  [M] input token was not the mask */
+  DLM_GET_KCACHE = 12,   /* dtype  [L][batch][n_kv_heads][seq_len][head_dim] */
+  DLM_GET_VCACHE = 13    /* same layout */
+};
+int dlm_get(dlm_handle* h, int32_t what, const void** dev_ptr, int64_t* n);
+
+/* Host-side counters of the last dlm_step: its step index and algorithmic
+ * FLOPs (sum over the GEMM and attention launches it made). */
+int dlm_last_step_info(const dlm_handle* h, int32_t* step, int32_t* m_tot, double* flops);
+
+/* Frees the handle (not state_mem).  Waits for the stream. */
+int dlm_destroy(dlm_handle* h);
+
+const char* dlm_error_string(int status);
+
+/* Per-kernel-class timing with HIP events recorded on the handle's stream
+ * around each launch (off by default).  Classes: */
+enum {
+  DLM_K_COMPACT = 0, DLM_K_EMBED_NORM, DLM_K_RMSNORM, DLM_K_GEMM_QKV, DLM_K_ROPE_KV,
+  DLM_K_ATTENTION, DLM_K_GEMM_O, DLM_K_GEMM_GATE_UP, DLM_K_GEMM_DOWN, DLM_K_GEMM_LM_HEAD,
+  DLM_K_VOCAB_STATS, DLM_K_COMMIT_LOCK, DLM_K_NUM_CLASSES
+};
+/* on != 0 starts timing (and clears the accumulators). */
+int dlm_set_timing(dlm_handle* h, int32_t on);
+/* Synchronises, then returns the summed event time (ms), launch count and
+ * summed algorithmic bytes and FLOPs of a class since timing was switched on. */
+int dlm_read_timing(dlm_handle* h, int32_t kclass, double* total_ms, int64_t* launches,
+                    double* bytes, double* flops);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLM_H */

@@ -1,0 +1,135 @@
+/*
+ * dlm_ops.h -- op-level C ABI: each call launches one stage of the denoising
+ * step (the same kernels and launch plans dlm_step uses) on caller buffers.
+ * Used for kernel-level parity and for timing one layer in isolation.
+ *
+ * Conventions as in dlm.h: int status, host-side validation before any
+ * launch, no allocation, all pointers are device memory unless stated,
+ * launches on `stream` (a hipStream_t; NULL = default stream), asynchronous.
+ * dtype is DLM_FP32 or DLM_BF16 (bf16 as uint16); "dtype" arrays below use
+ * that element type.  Workspace sizes come from the *_ws_bytes queries; a
+ * call given at least that much uses the same launch plan as dlm_step.
+ */
+#ifndef DLM_OPS_H
+#define DLM_OPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dlm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Active-set compaction (SureLock page, §2 core mechanism: a locked position
+ * leaves the active set A_t for good).  bits: uint64 [batch][ceil(seq_len/64)],
+ * bit (pos % 64) of word pos/64 set = locked.  Writes the active rows in
+ * ascending (seq, pos) order: row_seq, row_pos int32 [<= batch*seq_len];
+ * m_b int32 [batch] (rows per sequence); row_start int32 [batch+1] (prefix
+ * of m_b); ctl int32 [4]: ctl[0] = total rows M (ctl[1..3] untouched). */
+int dlm_op_compact(const uint64_t* bits, int32_t batch, int32_t seq_len, int32_t* row_seq,
+                   int32_t* row_pos, int32_t* m_b, int32_t* row_start, int32_t* ctl,
+                   void* stream);
+
+/* Embedding gather + RMSNorm for the active rows (SureLock page, §2: locked
+ * positions get no compute at all).  tokens int32 [batch][seq_len]; emb
+ * dtype [vocab][d]; g dtype [d].  Writes h float [M][d] = emb[token],
+ * y dtype [M][d] = h / sqrt(mean(h^2) + eps) * g, row_real int32 [M] =
+ * (token != mask_id). */
+int dlm_op_embed_rmsnorm(int32_t dtype, int32_t M, int32_t d, int32_t seq_len, float eps,
+                         int32_t mask_id, const int32_t* tokens, const int32_t* row_seq,
+                         const int32_t* row_pos, const void* emb, const void* g, float* h,
+                         void* y, int32_t* row_real, void* stream);
+
+/* y dtype [M][d] = x / sqrt(mean(x^2) + eps) * g; x float [M][d]. */
+int dlm_op_rmsnorm(int32_t dtype, int32_t M, int32_t d, float eps, const float* x,
+                   const void* g, void* y, void* stream);
+
+/* GEMM epilogues. */
+enum {
+  DLM_EPI_STORE_F32 = 0, /* C float [M][N] = A W^T */
+  DLM_EPI_RESID_ADD = 1, /* C float [M][N] += A W^T (the residual stream) */
+  DLM_EPI_SWIGLU = 2,    /* C dtype [M][N] = silu(A W^T) * (A W2^T), silu(x) = x/(1+e^-x) */
+  DLM_EPI_LOGITS = 3     /* C float, row r stored at (row_seq[r]*seq_len + row_pos[r])*N;
+                            column mask_id set to -inf */
+};
+/* Active-row GEMM on ragged M (SureLock page, §2: query projection and FFN
+ * only for active rows; FFN cost O(M d^2)).  A dtype [M][K] row-major, W (and
+ * W2 for SWIGLU) dtype [N][K].  Requires M >= 0, N > 0, K > 0 (bf16 fast
+ * path: K % 64 == 0; other shapes take the generic kernel). */
+size_t dlm_op_gemm_ws_bytes(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K);
+int dlm_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A,
+                const void* W, const void* W2, void* C, const int32_t* row_seq,
+                const int32_t* row_pos, int32_t seq_len, int32_t mask_id, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* Rotary table float [seq_len][head_dim/2][2] = (cos, sin) of
+ * pos * base^(-2j/head_dim), computed in double on the device. */
+int dlm_op_rope_table(int32_t seq_len, int32_t head_dim, float base, float* table,
+                      void* stream);
+
+/* Rotary embedding of q and k at each row's position, then K/V scatter into
+ * the cache (SureLock page, §2: K and V of positions are cached; fresh
+ * Q/K/V exist only for the active subset).  qkv float [M][(nq+2nkv)hd];
+ * table from dlm_op_rope_table or NULL (no rotation).  Writes q dtype
+ * [M][nq hd] and, for each row, kcache/vcache dtype [batch][nkv][seq_len][hd]
+ * at (row_seq, kv head, row_pos); other cache entries are untouched. */
+int dlm_op_rope_scatter(int32_t dtype, int32_t M, int32_t nq, int32_t nkv, int32_t hd,
+                        int32_t seq_len, const float* qkv, const int32_t* row_seq,
+                        const int32_t* row_pos, const float* table, void* q, void* kcache,
+                        void* vcache, void* stream);
+
+/* Attention of the active queries over every cached position of their
+ * sequence, non-causal (SureLock page, §2 continued attention; cost
+ * O(M N d)): o[r][h] = sum_j softmax_j(q[r][h].k[j] / sqrt(hd)) v[j] over
+ * j < seq_len, K/V head h*nkv/nq.  q dtype [M][nq hd]; rows of sequence b are
+ * rows [row_start[b], row_start[b+1]) (row_start int32 [batch+1], as written
+ * by dlm_op_compact); o dtype [M][nq hd]. */
+size_t dlm_op_attention_ws_bytes(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len,
+                                 int32_t nq, int32_t nkv, int32_t hd);
+int dlm_op_attention(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, int32_t nq,
+                     int32_t nkv, int32_t hd, const void* q, const int32_t* row_start,
+                     const void* kcache, const void* vcache, void* o, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Vocabulary statistics of the active rows (SureLock page, §2 locking
+ * condition: KL between the current and previous posterior, confidence
+ * gate).  Logits live per position: z_cur/z_prev float [batch][seq_len][V],
+ * row r at (row_seq[r], row_pos[r]).  For each row, over v != mask_id:
+ * lse = log sum e^z; argmax = smallest v with the largest z; conf =
+ * e^{z_argmax - lse}; if has_prev[pos]: kl = KL(p_t||p_{t-1}) (kl_dir 0) or
+ * KL(p_{t-1}||p_t) (kl_dir 1), where log p_{t-1} = z_prev - lse_prev[pos].
+ * Writes per row argmax, conf, kl (NaN without previous), has_kl, lse_row;
+ * per position lse_cur[pos] = lse and has_prev[pos] = 1.  A non-finite lse
+ * sets *err = 1. */
+size_t dlm_op_vocab_ws_bytes(int32_t M, int32_t V);
+int dlm_op_vocab_stats(int32_t M, int32_t V, int32_t mask_id, int32_t kl_dir, int32_t seq_len,
+                       const int32_t* row_seq, const int32_t* row_pos, const float* z_cur,
+                       const float* z_prev, const float* lse_prev, int32_t* has_prev,
+                       float* lse_cur, int32_t* argmax, float* conf, float* kl,
+                       int32_t* has_kl, float* lse_row, int32_t* err, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Commit + lock transition of one step (SlowFast page §1/§2: confidence-
+ * ranked top-k unmasking in semi-autoregressive blocks; SureLock page §2:
+ * KL lock test with confidence gate, permanent deactivation).  Per sequence:
+ * among its rows whose token is mask_id and whose position is in
+ * [blk_lo, blk_hi), the k with the largest conf (ties: smaller position)
+ * take their argmax (if do_commit).  If do_lock and policy == DLM_LOCK_TEST:
+ * each row passes iff row_real && has_kl && kl <= kl_eps && conf >= conf_tau;
+ * counter = pass ? counter + 1 : 0; lock bit set when counter >= n_consec.
+ * lock_prompt != 0 additionally locks positions [0, prompt_len). */
+int dlm_op_commit_lock(int32_t batch, int32_t seq_len, int32_t prompt_len, int32_t mask_id,
+                       int32_t blk_lo, int32_t blk_hi, int32_t k, int32_t do_commit,
+                       int32_t do_lock, int32_t policy, float kl_eps, float conf_tau,
+                       int32_t n_consec, int32_t lock_prompt, const int32_t* row_seq,
+                       const int32_t* row_pos, const int32_t* row_start,
+                       const int32_t* row_real, const int32_t* argmax, const float* conf,
+                       const float* kl, const int32_t* has_kl, int32_t* tokens,
+                       uint64_t* bits, int32_t* counters, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLM_OPS_H */

@@ -286,9 +286,9 @@ void lock_transition(const orc_model& m, const orc_run& r, int t, int M,
                      const int32_t* argmax, const double* conf, const double* kl,
                      const uint8_t* has_kl, int32_t* x, uint8_t* locked, int32_t* cnt,
                      std::vector<int32_t>* cseq, std::vector<int32_t>* cpos,
-                     std::vector<int32_t>* ctok) {
+                     std::vector<int32_t>* ctok, bool do_commit = true, bool do_lock = true) {
   const int N = r.seq_len;
-  const Sched sc = schedule(r, t);
+  const Sched sc = do_commit ? schedule(r, t) : Sched{-1, 0, 0, 0};
   // Commit: among this step's rows whose token is still the mask and which
   // lie in the current block, the k most confident take their argmax
   // (ties: smaller position first).
@@ -314,7 +314,7 @@ void lock_transition(const orc_model& m, const orc_run& r, int t, int M,
   // Lock test: a row with a real input token passes when its KL is defined,
   // at most eps, and its confidence is at least tau; n_consec consecutive
   // passes lock it for good.
-  if (r.policy == 1) {
+  if (do_lock && r.policy == 1) {
     for (int i = 0; i < M; ++i) {
       const size_t p = (size_t)row_seq[i] * N + row_pos[i];
       const bool pass = row_real[i] && has_kl[i] && kl[i] <= r.kl_eps && conf[i] >= r.conf_tau;
@@ -515,9 +515,10 @@ int orc_step_sample(orc_state* s, const int32_t* sample_rows, int n_sample) {
 
 int orc_step(orc_state* s) { return orc_step_sample(s, nullptr, -1); }
 
-// State transition after a step: commit + lock test.  With an override the
-// given commits replace the top-k choice, and/or the given lock bits and
-// counters replace the lock test's result (used to replay near-tie decisions).
+// State transition after a step: commit + lock test.  An override replaces
+// a decision instead of the rule: given commits replace the top-k choice;
+// given lock bits replace the lock test (locked |= bits, counters set from
+// ov_cnt when given, else kept).  Used to replay near-tie decisions.
 int orc_lock_update(orc_state* s, const int32_t* ov_commit_seq, const int32_t* ov_commit_pos,
                     const int32_t* ov_commit_tok, int32_t n_ov_commit,
                     const uint8_t* ov_locked /* [B][N] or null */,
@@ -527,13 +528,12 @@ int orc_lock_update(orc_state* s, const int32_t* ov_commit_seq, const int32_t* o
   s->commit_seq.clear();
   s->commit_pos.clear();
   s->commit_tok.clear();
-  std::vector<int32_t> x0 = s->x;
+  const bool ov_commit = n_ov_commit >= 0, ov_lock = ov_locked != nullptr;
   lock_transition(s->m, r, s->t, s->M, s->row_seq.data(), s->row_pos.data(), s->row_real.data(),
                   s->row_argmax.data(), s->row_conf.data(), s->row_kl.data(),
                   s->row_has_kl.data(), s->x.data(), s->locked.data(), s->cnt.data(),
-                  &s->commit_seq, &s->commit_pos, &s->commit_tok);
-  if (n_ov_commit >= 0) {
-    s->x = x0;
+                  &s->commit_seq, &s->commit_pos, &s->commit_tok, !ov_commit, !ov_lock);
+  if (ov_commit) {
     s->commit_seq.assign(ov_commit_seq, ov_commit_seq + n_ov_commit);
     s->commit_pos.assign(ov_commit_pos, ov_commit_pos + n_ov_commit);
     s->commit_tok.assign(ov_commit_tok, ov_commit_tok + n_ov_commit);
@@ -541,9 +541,10 @@ int orc_lock_update(orc_state* s, const int32_t* ov_commit_seq, const int32_t* o
       s->x[(size_t)ov_commit_seq[j] * r.seq_len + ov_commit_pos[j]] = ov_commit_tok[j];
   }
   const size_t BN = (size_t)r.batch * r.seq_len;
-  if (ov_locked)
+  if (ov_lock) {
     for (size_t p = 0; p < BN; ++p) s->locked[p] = s->locked[p] | (ov_locked[p] ? 1 : 0);
-  if (ov_cnt) std::memcpy(s->cnt.data(), ov_cnt, sizeof(int32_t) * BN);
+    if (ov_cnt) std::memcpy(s->cnt.data(), ov_cnt, sizeof(int32_t) * BN);
+  }
   s->t += 1;
   s->stepped = false;
   return 0;

@@ -1,0 +1,81 @@
+// Host-side launchers of the engine's kernels (one per stage of the step).
+// Each takes device pointers and a stream, validates nothing (the C ABI
+// layer does) and returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dlm {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+enum Epi { kEpiStoreF32 = 0, kEpiResidAdd = 1, kEpiSwiglu = 2, kEpiLogits = 3 };
+
+// ---- compaction -------------------------------------------------------------
+hipError_t launch_compact(const uint64_t* bits, int B, int N, int32_t* row_seq, int32_t* row_pos,
+                          int32_t* m_b, int32_t* row_start, int32_t* ctl, hipStream_t s);
+
+// ---- norms / embedding / rotary ----------------------------------------------
+hipError_t launch_embed_rmsnorm(int dtype, int M, int d, int N, float eps, int mask_id,
+                                const int32_t* tokens, const int32_t* row_seq,
+                                const int32_t* row_pos, const void* emb, const void* g, float* h,
+                                void* y, int32_t* row_real, hipStream_t s);
+hipError_t launch_rmsnorm(int dtype, int M, int d, float eps, const float* x, const void* g,
+                          void* y, hipStream_t s);
+hipError_t launch_rope_table(int N, int hd, float base, float* table, hipStream_t s);
+hipError_t launch_rope_scatter(int dtype, int M, int nq, int nkv, int hd, int N, const float* qkv,
+                               const int32_t* row_seq, const int32_t* row_pos,
+                               const float* table, void* q, void* kc, void* vc, hipStream_t s);
+
+// ---- GEMM ---------------------------------------------------------------------
+struct GemmArgs {
+  int dtype, epi, M, N, K;
+  const void* A;
+  const void* W;
+  const void* W2;
+  void* C;
+  const int32_t* row_seq;
+  const int32_t* row_pos;
+  int seq_len, mask_id;
+};
+size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K);
+hipError_t launch_gemm(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+
+// ---- attention -----------------------------------------------------------------
+size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd);
+hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int hd,
+                            const void* q, const int32_t* row_start, const void* kc,
+                            const void* vc, void* o, void* ws, size_t ws_bytes, hipStream_t s);
+
+// ---- vocabulary statistics ----------------------------------------------------------
+size_t vocab_ws_bytes(int M, int V);
+hipError_t launch_vocab_stats(int M, int V, int mask_id, int kl_dir, int N,
+                              const int32_t* row_seq, const int32_t* row_pos,
+                              const float* z_cur, const float* z_prev, const float* lse_prev,
+                              int32_t* has_prev, float* lse_cur, int32_t* argmax, float* conf,
+                              float* kl, int32_t* has_kl, float* lse_row, int32_t* err,
+                              void* ws, size_t ws_bytes, hipStream_t s);
+
+// ---- commit + lock -------------------------------------------------------------------
+struct LockArgs {
+  int B, N, P, mask_id, blk_lo, blk_hi, k, do_commit, do_lock, policy;
+  float kl_eps, conf_tau;
+  int n_consec, lock_prompt;
+  const int32_t *row_seq, *row_pos, *row_start, *row_real, *argmax;
+  const float *conf, *kl;
+  const int32_t* has_kl;
+  int32_t* tokens;
+  uint64_t* bits;
+  int32_t* counters;
+};
+hipError_t launch_commit_lock(const LockArgs& a, hipStream_t s);
+hipError_t launch_apply_override(int B, int N, int n_commit, const int32_t* cseq,
+                                 const int32_t* cpos, const int32_t* ctok, const uint64_t* bits_or,
+                                 const int32_t* counters, int32_t* tokens, uint64_t* bits,
+                                 int32_t* cnt, hipStream_t s);
+hipError_t launch_init_state(int B, int N, int P, int mask_id, const int32_t* prompts,
+                             int32_t* tokens, uint64_t* bits, int32_t* counters,
+                             int32_t* has_prev, int32_t* ctl, hipStream_t s);
+
+}  // namespace dlm

@@ -1,0 +1,345 @@
+// Attention of the M active queries over all N cached positions.
+//
+// SureLock page ("Stopping Computation for Converged Tokens in Masked
+// Diffusion-LM Decoding"), §2 Methodology, continued attention: active
+// (unlocked) tokens still attend to the locked ones through their cached K/V
+// while fresh Q/K/V exist only for the active subset; attention cost is
+// O(M_t N d) (§2 algorithmic complexity).  Non-causal: every query sees every
+// position of its sequence.  §5 names fused kernels and a contiguous cache
+// layout as the way to turn the FLOP saving into wall-clock; the cache here
+// is head-major [seq][kv head][pos][hd], so one (seq, kv head) is one
+// contiguous N x hd slab that a workgroup streams through LDS.
+//
+// MFMA kernel (bf16, hd in {64, 128}): a workgroup owns 64 query vectors of
+// one (seq, kv head) -- (row, query head) pairs, so GQA groups share the K/V
+// stream -- 16 per wave, and walks the keys in tiles of 64:
+//   S^T = K Q^T   with v_mfma_f32_16x16x32_bf16 (K from LDS, Q in registers);
+//                 lane l then holds S[key 4(l/16)+i][query l%16];
+//   online softmax per query column (exp2 domain, max/sum over the 4 lanes
+//                 sharing l%16);
+//   O^T += V^T P^T with v_mfma_f32_16x16x16_bf16: the S^T registers are
+//                 already the B operand; V^T comes from a transposed LDS copy.
+// Split-KV (gridDim.z > 1) writes unnormalised partials (o, max, sum) that a
+// combine pass merges by log-sum-exp.
+#include "common.h"
+#include "internal.h"
+
+namespace dlm {
+
+constexpr int kAttnQ = 64;     // query vectors per workgroup
+constexpr int kAttnKeys = 64;  // keys per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int HD, bool SPLIT>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ row_start,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ o, int N,
+    int nq, int nkv, int keys_per_split, int M, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  constexpr int KP = HD + 8;          // K tile pitch (elements)
+  constexpr int VP = kAttnKeys + 4;   // V^T tile pitch (elements)
+  constexpr int NKC = HD / 32;        // 32-wide hd chunks for S
+  constexpr int NCB = HD / 16;        // 16-wide hd blocks for O
+  __shared__ __attribute__((aligned(16))) bf16_t sK[kAttnKeys * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[HD * VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bg = blockIdx.y;
+  const int b = bg / nkv, g = bg % nkv;
+  const int G = nq / nkv;
+  const int r0 = row_start[b], Mb = row_start[b + 1] - r0;
+  const int Qn = Mb * G;
+  const int qbase = blockIdx.x * kAttnQ;
+  if (qbase >= Qn) return;
+
+  // this lane's query vector (column l%16 of the wave's 16)
+  const int qv = qbase + wave * 16 + (lane & 15);
+  const bool qok = qv < Qn;
+  const int row = r0 + (qok ? qv / G : 0);
+  const int head = g * G + (qok ? qv % G : 0);
+  bf16x8 qf[NKC];
+  {
+    const bf16_t* qp = q + (size_t)row * nq * HD + (size_t)head * HD + (lane >> 4) * 8;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      if (qok) {
+        qf[c] = *(const bf16x8*)(qp + c * 32);
+      } else {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        qf[c] = *(const bf16x8*)&z;
+      }
+    }
+  }
+
+  const size_t slab = ((size_t)b * nkv + g) * N * HD;
+  const bf16_t* kslab = kc + slab;
+  const bf16_t* vslab = vc + slab;
+  const int key0 = blockIdx.z * keys_per_split;
+  const int key1 = min(N, key0 + keys_per_split);
+  const float scale = kLog2e / sqrtf((float)HD);
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int CH = kAttnKeys * HD / 8;  // 16-byte chunks per tile
+  for (int t0 = key0; t0 < key1; t0 += kAttnKeys) {
+    __syncthreads();  // previous tile fully consumed
+    for (int c = tid; c < CH; c += 256) {
+      const int kr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
+      const int key = t0 + kr;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (key < key1) {
+        kv = *(const uint4*)(kslab + (size_t)key * HD + cc);
+        vv = *(const uint4*)(vslab + (size_t)key * HD + cc);
+      }
+      *(uint4*)&sK[kr * KP + cc] = kv;
+      const bf16_t* ve = (const bf16_t*)&vv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sVt[(cc + j) * VP + kr] = ve[j];
+    }
+    __syncthreads();
+
+    // S^T for the 4 key blocks of this tile
+    f32x4 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+        const bf16x8 a = *(const bf16x8*)&sK[(kb * 16 + (lane & 15)) * KP + c * 32 + (lane >> 4) * 8];
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[kb], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = t0 + kb * 16 + (lane >> 4) * 4 + i;
+        const float v = key < key1 ? s[kb][i] * scale : -INFINITY;
+        s[kb][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+    s16x4 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = (m_new == -INFINITY) ? 0.f : exp2f(s[kb][i] - m_new);
+        psum += p;
+        pb[kb][i] = (short)f2bf(p);
+      }
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      oacc[cb] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const s16x4 va =
+            *(const s16x4*)&sVt[(cb * 16 + (lane & 15)) * VP + kb * 16 + (lane >> 4) * 4];
+        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kb], oacc[cb], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!qok) return;
+  const int gq = row * nq + head;  // global query-vector id
+  if (SPLIT) {
+    const size_t base = (size_t)blockIdx.z * M * nq + gq;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part_o[base * HD + cb * 16 + (lane >> 4) * 4 + i] = oacc[cb][i];
+    if ((lane >> 4) == 0) {
+      part_ml[base * 2] = m_run;
+      part_ml[base * 2 + 1] = l_run;
+    }
+  } else {
+    const float inv = 1.f / l_run;
+    bf16_t* op = o + (size_t)row * nq * HD + (size_t)head * HD;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int c = cb * 16 + (lane >> 4) * 4;
+      ushort4 w;
+      w.x = f2bf(oacc[cb][0] * inv);
+      w.y = f2bf(oacc[cb][1] * inv);
+      w.z = f2bf(oacc[cb][2] * inv);
+      w.w = f2bf(oacc[cb][3] * inv);
+      *(ushort4*)(op + c) = w;
+    }
+  }
+}
+
+// Combine split-KV partials: o = sum_s o_s 2^(m_s - m) / sum_s l_s 2^(m_s - m).
+template <typename T>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           int splits, int MQ, int hd,
+                                                           T* __restrict__ o) {
+  const size_t total = (size_t)MQ * hd;
+  for (size_t f = blockIdx.x * (size_t)blockDim.x + threadIdx.x; f < total;
+       f += (size_t)gridDim.x * blockDim.x) {
+    const size_t gq = f / hd;
+    const int c = (int)(f % hd);
+    float m = -INFINITY;
+    for (int s = 0; s < splits; ++s) m = fmaxf(m, part_ml[((size_t)s * MQ + gq) * 2]);
+    float den = 0.f, num = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float ms = part_ml[((size_t)s * MQ + gq) * 2];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - m);
+      den += part_ml[((size_t)s * MQ + gq) * 2 + 1] * w;
+      num += part_o[((size_t)s * MQ + gq) * hd + c] * w;
+    }
+    st(o, f, num / den);
+  }
+}
+
+// Generic kernel (float or bf16, any even hd <= 256): one wave per
+// (row, query head); lanes split hd; keys visited in order with an online
+// softmax in fp32.
+template <typename T>
+__global__ __launch_bounds__(256) void attn_generic_kernel(
+    const T* __restrict__ q, const int32_t* __restrict__ row_start, int B,
+    const T* __restrict__ kc, const T* __restrict__ vc, T* __restrict__ o, int M, int N, int nq,
+    int nkv, int hd) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= M * nq) return;
+  const int row = gw / nq, h = gw % nq;
+  int b = 0;
+  while (b + 1 < B && row_start[b + 1] <= row) ++b;
+  const int g = h * nkv / nq;
+  const float scale = rsqrtf((float)hd);
+  float qv[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int col = lane + 64 * c;
+    qv[c] = col < hd ? ld(q, (size_t)row * nq * hd + (size_t)h * hd + col) * scale : 0.f;
+  }
+  const size_t slab = ((size_t)b * nkv + g) * N * hd;
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j < N; ++j) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = lane + 64 * c;
+      if (col < hd) s += qv[c] * ld(kc, slab + (size_t)j * hd + col);
+    }
+    s = wave_sum(s);
+    const float mn = fmaxf(m, s);
+    const float a = expf(m - mn), p = expf(s - mn);
+    l = l * a + p;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int col = lane + 64 * c;
+      acc[c] = acc[c] * a + (col < hd ? p * ld(vc, slab + (size_t)j * hd + col) : 0.f);
+    }
+    m = mn;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int col = lane + 64 * c;
+    if (col < hd) st(o, (size_t)row * nq * hd + (size_t)h * hd + col, acc[c] / l);
+  }
+}
+
+namespace {
+
+struct AttnPlan {
+  bool mfma;
+  int qtiles, splits, keys_per_split;
+  size_t ws;
+};
+
+AttnPlan make_attn_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd) {
+  AttnPlan p{};
+  p.mfma = dtype == kBF16 && (hd == 64 || hd == 128) && nq % nkv == 0;
+  p.splits = 1;
+  p.keys_per_split = N;
+  if (!p.mfma || M <= 0) return p;
+  const int G = nq / nkv;
+  const int mb_max = std::min(M, N);  // rows of one sequence
+  p.qtiles = (mb_max * G + kAttnQ - 1) / kAttnQ;
+  // estimated busy workgroups: the rows are spread over the sequences
+  const int busy = std::max(1, (M * G + kAttnQ - 1) / kAttnQ) * nkv;
+  const int ktiles = (N + kAttnKeys - 1) / kAttnKeys;
+  int splits = 1;
+  while (busy * splits < 512 && ktiles / (splits * 2) >= 1 &&
+         (size_t)(splits * 2) * M * nq * (hd + 2) * sizeof(float) <= (64ull << 20))
+    splits *= 2;
+  p.splits = splits;
+  p.keys_per_split = ((ktiles + splits - 1) / splits) * kAttnKeys;
+  p.ws = splits > 1 ? (size_t)splits * M * nq * (hd + 2) * sizeof(float) : 0;
+  return p;
+}
+
+template <int HD>
+hipError_t run_attn_mfma(const AttnPlan& p, int M, int B, int N, int nq, int nkv,
+                         const void* q, const int32_t* row_start, const void* kc,
+                         const void* vc, void* o, void* ws, hipStream_t s) {
+  dim3 grid(p.qtiles, B * nkv, p.splits);
+  if (p.splits > 1) {
+    float* po = (float*)ws;
+    float* pml = po + (size_t)p.splits * M * nq * HD;
+    attn_mfma_kernel<HD, true><<<grid, 256, 0, s>>>(
+        (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq,
+        nkv, p.keys_per_split, M, po, pml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t total = (size_t)M * nq * HD;
+    const int gsz = (int)std::min<size_t>((total + 255) / 256, 8192);
+    attn_combine_kernel<bf16_t><<<gsz, 256, 0, s>>>(po, pml, p.splits, M * nq, HD, (bf16_t*)o);
+  } else {
+    attn_mfma_kernel<HD, false><<<grid, 256, 0, s>>>(
+        (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq,
+        nkv, p.keys_per_split, M, nullptr, nullptr);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd) {
+  return make_attn_plan(dtype, M, B, N, nq, nkv, hd).ws;
+}
+
+hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int hd,
+                            const void* q, const int32_t* row_start, const void* kc,
+                            const void* vc, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  AttnPlan p = make_attn_plan(dtype, M, B, N, nq, nkv, hd);
+  if (p.mfma && p.ws > ws_bytes) {
+    p.splits = 1;
+    p.keys_per_split = N;
+  }
+  if (p.mfma) {
+    if (hd == 128) return run_attn_mfma<128>(p, M, B, N, nq, nkv, q, row_start, kc, vc, o, ws, s);
+    return run_attn_mfma<64>(p, M, B, N, nq, nkv, q, row_start, kc, vc, o, ws, s);
+  }
+  const int waves = M * nq;
+  const int grid = (waves + 3) / 4;
+  if (dtype == kBF16)
+    attn_generic_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)q, row_start, B,
+                                                     (const bf16_t*)kc, (const bf16_t*)vc,
+                                                     (bf16_t*)o, M, N, nq, nkv, hd);
+  else
+    attn_generic_kernel<float><<<grid, 256, 0, s>>>((const float*)q, row_start, B,
+                                                    (const float*)kc, (const float*)vc,
+                                                    (float*)o, M, N, nq, nkv, hd);
+  return hipGetLastError();
+}
+
+}  // namespace dlm

@@ -1,0 +1,209 @@
+// Posterior statistics of the active rows over the vocabulary.
+//
+// SureLock page ("Stopping Computation for Converged Tokens in Masked
+// Diffusion-LM Decoding"), §2 Methodology, locking condition: the primary
+// criterion is the step-wise divergence D = KL(p_t || p_{t-1}) between the
+// current and previous posterior of a position, with an optional gate that
+// the token is also highly confident.  Confidence here is the max
+// probability; the argmax is the token a commit would write.
+//
+// One pass reads the current logits z and, where a previous posterior
+// exists, the previous logits z' (the engine keeps each position's logits of
+// the last step, double-buffered by step parity, plus that step's
+// log-normaliser lse').  With an online max m it accumulates
+//   S0 = sum e^{z-m},  S1 = sum e^{z-m} (z - z'),   (KL(p_t || p_{t-1}))
+//   T1 = sum q (z' - z), q = e^{z' - lse'}          (KL(p_{t-1} || p_t))
+// so that lse = m + log S0, conf = 1/S0 and
+//   KL(p_t || p_{t-1}) = S1/S0 - (lse - lse'),  KL(p_{t-1} || p_t) = T1 + lse - lse'.
+// The mask token's column is excluded (probability 0).  Rows are split over
+// several workgroups (chunks of the vocabulary); a second pass merges the
+// chunk partials per row.
+#include "common.h"
+#include "internal.h"
+
+namespace dlm {
+
+struct VPart {
+  float m, s0, s1, t1;
+  int am;
+};
+
+__device__ __forceinline__ VPart vmerge(VPart a, VPart b) {
+  VPart r;
+  r.m = fmaxf(a.m, b.m);
+  const float fa = (a.m == -INFINITY) ? 0.f : __expf(a.m - r.m);
+  const float fb = (b.m == -INFINITY) ? 0.f : __expf(b.m - r.m);
+  r.s0 = a.s0 * fa + b.s0 * fb;
+  r.s1 = a.s1 * fa + b.s1 * fb;
+  r.t1 = a.t1 + b.t1;
+  if (a.m > b.m) r.am = a.am;
+  else if (b.m > a.m) r.am = b.am;
+  else r.am = min(a.am, b.am);
+  return r;
+}
+
+constexpr int kVThreads = 256;
+
+template <int KLDIR>
+__global__ __launch_bounds__(kVThreads) void vocab_partial_kernel(
+    int V, int mask_id, int N, int chunk, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, const float* __restrict__ z_cur,
+    const float* __restrict__ z_prev, const float* __restrict__ lse_prev,
+    const int32_t* __restrict__ has_prev, VPart* __restrict__ part) {
+  __shared__ VPart red[kVThreads / 64];
+  const int r = blockIdx.y, c = blockIdx.x, nchunks = gridDim.x;
+  const size_t slot = (size_t)row_seq[r] * N + row_pos[r];
+  const float* z = z_cur + slot * V;
+  const float* zp = z_prev + slot * V;
+  const bool hp = has_prev[slot] != 0;
+  const float lsep = hp ? lse_prev[slot] : 0.f;
+  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+
+  VPart acc{-INFINITY, 0.f, 0.f, 0.f, 0x7fffffff};
+  auto visit = [&](int v, float zv, float zpv) {
+    if (v == mask_id || zv == -INFINITY) {
+      if (KLDIR == 1 && hp && v != mask_id) {
+        const float q = __expf(zpv - lsep);
+        if (q > 0.f) acc.t1 += q * (zpv - zv);
+      }
+      return;
+    }
+    const float d = zv - zpv;
+    if (zv > acc.m) {
+      const float sc = (acc.m == -INFINITY) ? 0.f : __expf(acc.m - zv);
+      acc.s0 = acc.s0 * sc + 1.f;
+      if (KLDIR == 0) acc.s1 = acc.s1 * sc + (hp ? d : 0.f);
+      acc.m = zv;
+      acc.am = v;
+    } else {
+      const float e = __expf(zv - acc.m);
+      acc.s0 += e;
+      if (KLDIR == 0 && hp) acc.s1 += e * d;
+    }
+    if (KLDIR == 1 && hp) {
+      const float q = __expf(zpv - lsep);
+      if (q > 0.f) acc.t1 += q * (zpv - zv);
+    }
+  };
+  // each thread visits its elements in increasing v, so a strict '>' keeps
+  // the smallest index among equal maxima
+  const bool vec = ((V & 3) == 0) && ((v0 & 3) == 0);
+  if (vec) {
+    const int n4 = (v1 - v0) >> 2;
+    const float4* z4 = (const float4*)(z + v0);
+    const float4* zp4 = (const float4*)(zp + v0);
+    for (int i = threadIdx.x; i < n4; i += kVThreads) {
+      const float4 a = z4[i];
+      const float4 p = hp ? zp4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int v = v0 + 4 * i;
+      visit(v, a.x, p.x);
+      visit(v + 1, a.y, p.y);
+      visit(v + 2, a.z, p.z);
+      visit(v + 3, a.w, p.w);
+    }
+    for (int v = v0 + 4 * n4 + threadIdx.x; v < v1; v += kVThreads)
+      visit(v, z[v], hp ? zp[v] : 0.f);
+  } else {
+    for (int v = v0 + threadIdx.x; v < v1; v += kVThreads) visit(v, z[v], hp ? zp[v] : 0.f);
+  }
+  // wave merge then cross-wave merge
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    VPart b;
+    b.m = __shfl_xor(acc.m, o, 64);
+    b.s0 = __shfl_xor(acc.s0, o, 64);
+    b.s1 = __shfl_xor(acc.s1, o, 64);
+    b.t1 = __shfl_xor(acc.t1, o, 64);
+    b.am = __shfl_xor(acc.am, o, 64);
+    acc = vmerge(acc, b);
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) red[w] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    VPart t = red[0];
+    for (int i = 1; i < kVThreads / 64; ++i) t = vmerge(t, red[i]);
+    part[(size_t)r * nchunks + c] = t;
+  }
+}
+
+// One thread per row: merge chunk partials (in chunk order), finish the
+// statistics, record lse for the next step, latch non-finite results.
+__global__ void vocab_merge_kernel(int M, int nchunks, int N, int kl_dir,
+                                   const int32_t* __restrict__ row_seq,
+                                   const int32_t* __restrict__ row_pos,
+                                   const float* __restrict__ lse_prev,
+                                   int32_t* __restrict__ has_prev, float* __restrict__ lse_cur,
+                                   const VPart* __restrict__ part, int32_t* __restrict__ argmax,
+                                   float* __restrict__ conf, float* __restrict__ kl,
+                                   int32_t* __restrict__ has_kl, float* __restrict__ lse_row,
+                                   int32_t* __restrict__ err) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= M) return;
+  VPart t = part[(size_t)r * nchunks];
+  for (int c = 1; c < nchunks; ++c) t = vmerge(t, part[(size_t)r * nchunks + c]);
+  const size_t slot = (size_t)row_seq[r] * N + row_pos[r];
+  const float lse = t.m + logf(t.s0);
+  const bool hp = has_prev[slot] != 0;
+  argmax[r] = t.am;
+  conf[r] = 1.f / t.s0;
+  lse_row[r] = lse;
+  if (hp) {
+    const float dl = lse - lse_prev[slot];
+    kl[r] = kl_dir == 0 ? (t.s1 / t.s0 - dl) : (t.t1 + dl);
+    has_kl[r] = 1;
+  } else {
+    kl[r] = __int_as_float(0x7fc00000);
+    has_kl[r] = 0;
+  }
+  lse_cur[slot] = lse;
+  has_prev[slot] = 1;
+  if (!isfinite(lse)) atomicExch(err, 1);
+}
+
+namespace {
+struct VPlan { int chunks, chunk; };
+VPlan make_vplan(int M, int V) {
+  // aim for ~2048 workgroups, chunks of >= 1024 elements, <= 256 chunks
+  int chunks = std::max(1, (2048 + M - 1) / std::max(M, 1));
+  chunks = std::min(chunks, std::max(1, V / 1024));
+  chunks = std::min(chunks, 256);
+  int chunk = (V + chunks - 1) / chunks;
+  chunk = (chunk + 3) & ~3;
+  chunks = (V + chunk - 1) / chunk;
+  return VPlan{chunks, chunk};
+}
+}  // namespace
+
+size_t vocab_ws_bytes(int M, int V) {
+  if (M <= 0) return 0;
+  const VPlan p = make_vplan(M, V);
+  return (size_t)M * p.chunks * sizeof(VPart);
+}
+
+hipError_t launch_vocab_stats(int M, int V, int mask_id, int kl_dir, int N,
+                              const int32_t* row_seq, const int32_t* row_pos,
+                              const float* z_cur, const float* z_prev, const float* lse_prev,
+                              int32_t* has_prev, float* lse_cur, int32_t* argmax, float* conf,
+                              float* kl, int32_t* has_kl, float* lse_row, int32_t* err,
+                              void* ws, size_t ws_bytes, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  const VPlan p = make_vplan(M, V);
+  if ((size_t)M * p.chunks * sizeof(VPart) > ws_bytes) return hipErrorInvalidValue;
+  VPart* part = (VPart*)ws;
+  dim3 grid(p.chunks, M);
+  if (kl_dir == 0)
+    vocab_partial_kernel<0><<<grid, kVThreads, 0, s>>>(V, mask_id, N, p.chunk, row_seq, row_pos,
+                                                       z_cur, z_prev, lse_prev, has_prev, part);
+  else
+    vocab_partial_kernel<1><<<grid, kVThreads, 0, s>>>(V, mask_id, N, p.chunk, row_seq, row_pos,
+                                                       z_cur, z_prev, lse_prev, has_prev, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  vocab_merge_kernel<<<(M + 127) / 128, 128, 0, s>>>(M, p.chunks, N, kl_dir, row_seq, row_pos,
+                                                      lse_prev, has_prev, lse_cur, part, argmax,
+                                                      conf, kl, has_kl, lse_row, err);
+  return hipGetLastError();
+}
+
+}  // namespace dlm
