@@ -157,7 +157,7 @@ enum {
   DLM_GET_LOGITS = 10,   /* float  [batch][seq_len][vocab]; rows of this step's active positions */
   DLM_GET_ROW_REAL = 11, /* int32  [M] input token was not the mask */
   DLM_GET_KCACHE = 12,   /* dtype  [L][batch][n_kv_heads][seq_len][head_dim] */
-  DLM_GET_VCACHE = 13    /* same layout */
+  DLM_GET_VCACHE = 13    /* dtype  [L][batch][n_kv_heads][head_dim][seq_len] (transposed) */
 };
 int dlm_get(dlm_handle* h, int32_t what, const void** dev_ptr, int64_t* n);
 

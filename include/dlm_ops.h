@@ -56,13 +56,28 @@ enum {
 };
 /* Active-row GEMM on ragged M (SureLock page, §2: query projection and FFN
  * only for active rows; FFN cost O(M d^2)).  A dtype [M][K] row-major, W (and
- * W2 for SWIGLU) dtype [N][K].  Requires M >= 0, N > 0, K > 0 (bf16 fast
- * path: K % 64 == 0; other shapes take the generic kernel). */
+ * W2 for SWIGLU) dtype [N][K], all 16-byte aligned.  Requires M >= 0, N > 0,
+ * K > 0 (bf16 fast path: K % 64 == 0; other shapes take the generic kernel).
+ * When the plan splits K (dlm_op_gemm_ws_bytes > 0), fp32 partials go to ws
+ * and a second kernel sums them in split order.  Calls that share a
+ * workspace must not overlap. */
 size_t dlm_op_gemm_ws_bytes(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K);
 int dlm_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, const void* A,
                 const void* W, const void* W2, void* C, const int32_t* row_seq,
                 const int32_t* row_pos, int32_t seq_len, int32_t mask_id, void* ws,
                 size_t ws_bytes, void* stream);
+
+/* The same GEMM with a forced launch configuration, for tuning and for
+ * testing every configuration the plan can choose: cfg indexes the bf16 MFMA
+ * tile table (dlm_op_gemm_num_configs() entries; < 0 = the default plan),
+ * splits > 0 forces the split-K factor.  Needs ws of at least
+ * splits*M*N*4 bytes (2x for SWIGLU) when splits > 1. */
+int dlm_op_gemm_num_configs(void);
+int dlm_op_gemm_config(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K,
+                       const void* A, const void* W, const void* W2, void* C,
+                       const int32_t* row_seq, const int32_t* row_pos, int32_t seq_len,
+                       int32_t mask_id, int32_t cfg, int32_t splits, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Rotary table float [seq_len][head_dim/2][2] = (cos, sin) of
  * pos * base^(-2j/head_dim), computed in double on the device. */
@@ -73,8 +88,10 @@ int dlm_op_rope_table(int32_t seq_len, int32_t head_dim, float base, float* tabl
  * the cache (SureLock page, §2: K and V of positions are cached; fresh
  * Q/K/V exist only for the active subset).  qkv float [M][(nq+2nkv)hd];
  * table from dlm_op_rope_table or NULL (no rotation).  Writes q dtype
- * [M][nq hd] and, for each row, kcache/vcache dtype [batch][nkv][seq_len][hd]
- * at (row_seq, kv head, row_pos); other cache entries are untouched. */
+ * [M][nq hd] and, for each row, kcache dtype [batch][nkv][seq_len][hd] at
+ * (row_seq, kv head, row_pos) and vcache dtype [batch][nkv][hd][seq_len]
+ * (transposed) at (row_seq, kv head, :, row_pos); other cache entries are
+ * untouched. */
 int dlm_op_rope_scatter(int32_t dtype, int32_t M, int32_t nq, int32_t nkv, int32_t hd,
                         int32_t seq_len, const float* qkv, const int32_t* row_seq,
                         const int32_t* row_pos, const float* table, void* q, void* kcache,
@@ -83,7 +100,8 @@ int dlm_op_rope_scatter(int32_t dtype, int32_t M, int32_t nq, int32_t nkv, int32
 /* Attention of the active queries over every cached position of their
  * sequence, non-causal (SureLock page, §2 continued attention; cost
  * O(M N d)): o[r][h] = sum_j softmax_j(q[r][h].k[j] / sqrt(hd)) v[j] over
- * j < seq_len, K/V head h*nkv/nq.  q dtype [M][nq hd]; rows of sequence b are
+ * j < seq_len, K/V head h*nkv/nq.  q dtype [M][nq hd]; kcache [batch][nkv]
+ * [seq_len][hd], vcache [batch][nkv][hd][seq_len]; rows of sequence b are
  * rows [row_start[b], row_start[b+1]) (row_start int32 [batch+1], as written
  * by dlm_op_compact); o dtype [M][nq hd]. */
 size_t dlm_op_attention_ws_bytes(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len,

@@ -125,7 +125,7 @@ Layout make_layout(const dlm_model_desc& m, const dlm_run_desc& r) {
   L.q = take(BN * qo * es);
   L.o = take(BN * qo * es);
   L.u = take(BN * (size_t)m.d_ff * es);
-  L.ws_bytes = max_ws(m, r);
+  L.ws_bytes = std::max<size_t>(max_ws(m, r), 256);
   L.ws = take(L.ws_bytes);
   L.ov_cseq = take(BN * 4);
   L.ov_cpos = take(BN * 4);
@@ -367,29 +367,50 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out) {
                                 row_seq, row_pos, h->emb, h->attn_norm[0], hres, a,
                                 h->at<int32_t>(y.row_real), s);
   }));
+  // GEMM launch with its algorithmic work; `deferred` (float-store and
+  // residual epilogues) leaves split-K partials in ws for the next kernel
+  // and returns the split count through *splits.
   auto gemm = [&](int cls, int epi, int Nn, int K, const void* A, const void* W, const void* W2,
-                  void* C) {
-    GemmArgs g{dt, epi, M, Nn, K, A, W, W2, C, row_seq, row_pos, N, m.mask_id};
+                  void* C, int* splits) {
+    GemmArgs g{dt, epi, M, Nn, K, A, W, W2, C, row_seq, row_pos, N, m.mask_id,
+               nullptr, nullptr, nullptr, nullptr, 0, 0};
     const double mats = epi == kEpiSwiglu ? 2.0 : 1.0;
     const double fl = 2.0 * M * (double)Nn * K * mats;
     const double out_b = epi == kEpiSwiglu ? es : (epi == kEpiResidAdd ? 8.0 : 4.0);
     const double by = mats * Nn * (double)K * es + M * (double)K * es + M * (double)Nn * out_b;
     h->flops += fl;
-    return timed(h, cls, by, fl, [&] { return launch_gemm(g, ws, y.ws_bytes, s); });
+    return timed(h, cls, by, fl, [&] {
+      if (splits) return launch_gemm_deferred(g, ws, y.ws_bytes, s, splits);
+      return launch_gemm(g, ws, y.ws_bytes, s);
+    });
   };
+  const float* part = (const float*)ws;
+  int sp_res = 0;  // split-K partials of the last residual update, pending
   for (int l = 0; l < m.n_layers; ++l) {
     if (l > 0)
       TRY(timed(h, DLM_K_RMSNORM, M * (double)d * (4 + es), 0.0, [&] {
-        return launch_rmsnorm(dt, M, d, m.rms_eps, hres, h->attn_norm[l], a, s);
+        return launch_rmsnorm_resid(dt, M, d, m.rms_eps, hres, part, sp_res, h->attn_norm[l], a,
+                                    s);
       }));
-    TRY(gemm(DLM_K_GEMM_QKV, kEpiStoreF32, qkv_out, d, a, h->w_qkv[l], nullptr, qkv));
     unsigned char* kcl = h->base + y.kc + l * kv_layer;
     unsigned char* vcl = h->base + y.vc + l * kv_layer;
-    TRY(timed(h, DLM_K_ROPE_KV, M * (double)qkv_out * (4 + es), 0.0, [&] {
-      return launch_rope_scatter(dt, M, nq, nkv, hd, N, qkv, row_seq, row_pos,
-                                 m.rope_base > 0.f ? h->at<float>(y.rope) : nullptr, q, kcl, vcl,
-                                 s);
-    }));
+    const float* rope = m.rope_base > 0.f ? h->at<float>(y.rope) : nullptr;
+    if (gemm_qkv_fusable(dt, M, hd, d)) {
+      // QKV projection with rotary embedding and cache scatter in its epilogue
+      GemmArgs g{dt, kEpiQKV, M, qkv_out, d, a, h->w_qkv[l], nullptr, nullptr, row_seq, row_pos,
+                 N, m.mask_id, rope, q, kcl, vcl, nq, nkv};
+      const double fl = 2.0 * M * (double)qkv_out * d;
+      const double by = qkv_out * (double)d * es + M * (double)d * es + M * (double)qkv_out * es;
+      h->flops += fl;
+      TRY(timed(h, DLM_K_GEMM_QKV, by, fl, [&] { return launch_gemm(g, ws, y.ws_bytes, s); }));
+    } else {
+      int sp_qkv = 0;
+      TRY(gemm(DLM_K_GEMM_QKV, kEpiStoreF32, qkv_out, d, a, h->w_qkv[l], nullptr, qkv, &sp_qkv));
+      TRY(timed(h, DLM_K_ROPE_KV, M * (double)qkv_out * (4 + es), 0.0, [&] {
+        return launch_rope_scatter_split(dt, M, nq, nkv, hd, N, qkv, part, sp_qkv, row_seq,
+                                         row_pos, rope, q, kcl, vcl, s);
+      }));
+    }
     {
       const double fl = 4.0 * M * (double)N * qo;
       const double by = 2.0 * kv_layer + 2.0 * M * (double)qo * es;
@@ -399,18 +420,18 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out) {
                                 y.ws_bytes, s);
       }));
     }
-    TRY(gemm(DLM_K_GEMM_O, kEpiResidAdd, d, qo, o, h->w_o[l], nullptr, hres));
+    TRY(gemm(DLM_K_GEMM_O, kEpiResidAdd, d, qo, o, h->w_o[l], nullptr, hres, &sp_res));
     TRY(timed(h, DLM_K_RMSNORM, M * (double)d * (4 + es), 0.0, [&] {
-      return launch_rmsnorm(dt, M, d, m.rms_eps, hres, h->ffn_norm[l], a, s);
+      return launch_rmsnorm_resid(dt, M, d, m.rms_eps, hres, part, sp_res, h->ffn_norm[l], a, s);
     }));
-    TRY(gemm(DLM_K_GEMM_GATE_UP, kEpiSwiglu, dff, d, a, h->w_gate[l], h->w_up[l], u));
-    TRY(gemm(DLM_K_GEMM_DOWN, kEpiResidAdd, d, dff, u, h->w_down[l], nullptr, hres));
+    TRY(gemm(DLM_K_GEMM_GATE_UP, kEpiSwiglu, dff, d, a, h->w_gate[l], h->w_up[l], u, nullptr));
+    TRY(gemm(DLM_K_GEMM_DOWN, kEpiResidAdd, d, dff, u, h->w_down[l], nullptr, hres, &sp_res));
   }
   TRY(timed(h, DLM_K_RMSNORM, M * (double)d * (4 + es), 0.0, [&] {
-    return launch_rmsnorm(dt, M, d, m.rms_eps, hres, h->fnorm, a, s);
+    return launch_rmsnorm_resid(dt, M, d, m.rms_eps, hres, part, sp_res, h->fnorm, a, s);
   }));
   float* zc = h->at<float>(y.z[cur]);
-  TRY(gemm(DLM_K_GEMM_LM_HEAD, kEpiLogits, V, d, a, h->lm, nullptr, zc));
+  TRY(gemm(DLM_K_GEMM_LM_HEAD, kEpiLogits, V, d, a, h->lm, nullptr, zc, nullptr));
   TRY(timed(h, DLM_K_VOCAB_STATS, M * (double)V * 8.0, 0.0, [&] {
     return launch_vocab_stats(M, V, m.mask_id, r.kl_dir, N, row_seq, row_pos, zc,
                               h->at<float>(y.z[prv]), h->at<float>(y.lse[prv]),
@@ -622,8 +643,31 @@ int dlm_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, con
   if (epi == kEpiLogits && (!row_seq || !row_pos || seq_len < 1)) return DLM_E_INVALID;
   auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   if (!al16(A) || !al16(W) || (W2 && !al16(W2))) return DLM_E_INVALID;
-  GemmArgs g{dtype, epi, M, N, K, A, W, W2, C, row_seq, row_pos, seq_len, mask_id};
+  GemmArgs g{dtype, epi, M, N, K, A, W, W2, C, row_seq, row_pos, seq_len, mask_id,
+             nullptr, nullptr, nullptr, nullptr, 0, 0};
   return hip_status(launch_gemm(g, ws, ws ? ws_bytes : 0, (hipStream_t)stream));
+}
+
+int dlm_op_gemm_num_configs(void) { return gemm_num_configs(); }
+
+int dlm_op_gemm_config(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K,
+                       const void* A, const void* W, const void* W2, void* C,
+                       const int32_t* row_seq, const int32_t* row_pos, int32_t seq_len,
+                       int32_t mask_id, int32_t cfg, int32_t splits, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!dt_ok(dtype) || epi < 0 || epi > 3 || M < 0 || N < 1 || K < 1 || splits < 0 ||
+      cfg >= gemm_num_configs())
+    return DLM_E_INVALID;
+  if (M == 0) return DLM_OK;
+  if (!A || !W || !C || (epi == kEpiSwiglu && !W2)) return DLM_E_INVALID;
+  if (epi == kEpiLogits && (!row_seq || !row_pos || seq_len < 1)) return DLM_E_INVALID;
+  auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (!al16(A) || !al16(W) || (W2 && !al16(W2))) return DLM_E_INVALID;
+  if (splits > 1 && (size_t)splits * M * N * (epi == kEpiSwiglu ? 8 : 4) > ws_bytes)
+    return DLM_E_SIZE;
+  GemmArgs g{dtype, epi, M, N, K, A, W, W2, C, row_seq, row_pos, seq_len, mask_id,
+             nullptr, nullptr, nullptr, nullptr, 0, 0};
+  return hip_status(launch_gemm_cfg(g, cfg, splits, ws, ws ? ws_bytes : 0, (hipStream_t)stream));
 }
 
 int dlm_op_rope_table(int32_t seq_len, int32_t head_dim, float base, float* table,

@@ -10,7 +10,7 @@
 namespace dlm {
 
 enum Dtype { kF32 = 0, kBF16 = 1 };
-enum Epi { kEpiStoreF32 = 0, kEpiResidAdd = 1, kEpiSwiglu = 2, kEpiLogits = 3 };
+enum Epi { kEpiStoreF32 = 0, kEpiResidAdd = 1, kEpiSwiglu = 2, kEpiLogits = 3, kEpiQKV = 4 };
 
 // ---- compaction -------------------------------------------------------------
 hipError_t launch_compact(const uint64_t* bits, int B, int N, int32_t* row_seq, int32_t* row_pos,
@@ -23,10 +23,20 @@ hipError_t launch_embed_rmsnorm(int dtype, int M, int d, int N, float eps, int m
                                 void* y, int32_t* row_real, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, int M, int d, float eps, const float* x, const void* g,
                           void* y, hipStream_t s);
+// RMSNorm of the residual after it absorbs split-K partials [splits][M][d].
+hipError_t launch_rmsnorm_resid(int dtype, int M, int d, float eps, float* h,
+                                const float* partial, int splits, const void* g, void* y,
+                                hipStream_t s);
 hipError_t launch_rope_table(int N, int hd, float base, float* table, hipStream_t s);
 hipError_t launch_rope_scatter(int dtype, int M, int nq, int nkv, int hd, int N, const float* qkv,
                                const int32_t* row_seq, const int32_t* row_pos,
                                const float* table, void* q, void* kc, void* vc, hipStream_t s);
+// Same, with the QKV values given as split-K partials [splits][M][width].
+hipError_t launch_rope_scatter_split(int dtype, int M, int nq, int nkv, int hd, int N,
+                                     const float* qkv, const float* partial, int splits,
+                                     const int32_t* row_seq, const int32_t* row_pos,
+                                     const float* table, void* q, void* kc, void* vc,
+                                     hipStream_t s);
 
 // ---- GEMM ---------------------------------------------------------------------
 struct GemmArgs {
@@ -38,9 +48,30 @@ struct GemmArgs {
   const int32_t* row_seq;
   const int32_t* row_pos;
   int seq_len, mask_id;
+  // kEpiQKV only: rotary table [seq_len][hd/2][2] (or null), q out [M][nq hd],
+  // K cache [B][nkv][seq_len][hd], V cache transposed [B][nkv][hd][seq_len];
+  // hd must be 128.
+  const float* rope;
+  void* q;
+  void* kc;
+  void* vc;
+  int nq, nkv;
 };
 size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K);
 hipError_t launch_gemm(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+// For the float-store and residual-add epilogues: when the plan splits K, run
+// only the GEMM (partials [splits][M][N] in ws) and report the split count,
+// leaving the reduction to the consumer kernel; otherwise as launch_gemm with
+// *splits_out = 0.
+hipError_t launch_gemm_deferred(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s,
+                                int* splits_out);
+int gemm_num_configs();
+// QKV projection with rotary embedding and K/V cache scatter fused into the
+// epilogue (bf16, head_dim 128, K % 64 == 0); false if the shape is not
+// supported (then use kEpiStoreF32 + launch_rope_scatter).
+bool gemm_qkv_fusable(int dtype, int M, int hd, int K);
+hipError_t launch_gemm_cfg(const GemmArgs& a, int cfg, int splits, void* ws, size_t ws_bytes,
+                           hipStream_t s);
 
 // ---- attention -----------------------------------------------------------------
 size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd);

@@ -7,8 +7,9 @@
 // O(M_t N d) (§2 algorithmic complexity).  Non-causal: every query sees every
 // position of its sequence.  §5 names fused kernels and a contiguous cache
 // layout as the way to turn the FLOP saving into wall-clock; the cache here
-// is head-major [seq][kv head][pos][hd], so one (seq, kv head) is one
-// contiguous N x hd slab that a workgroup streams through LDS.
+// is head-major: K as [seq][kv head][pos][hd] and V transposed as
+// [seq][kv head][hd][pos], so one (seq, kv head) is two contiguous N x hd
+// slabs that a workgroup streams through LDS with plain 16-byte loads.
 //
 // MFMA kernel (bf16, hd in {64, 128}): a workgroup owns 64 query vectors of
 // one (seq, kv head) -- (row, query head) pairs, so GQA groups share the K/V
@@ -18,7 +19,8 @@
 //   online softmax per query column (exp2 domain, max/sum over the 4 lanes
 //                 sharing l%16);
 //   O^T += V^T P^T with v_mfma_f32_16x16x16_bf16: the S^T registers are
-//                 already the B operand; V^T comes from a transposed LDS copy.
+//                 already the B operand; V^T rows (keys contiguous) come
+//                 straight from the transposed cache.
 // Split-KV (gridDim.z > 1) writes unnormalised partials (o, max, sum) that a
 // combine pass merges by log-sum-exp.
 #include "common.h"
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     int nq, int nkv, int keys_per_split, int M, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   constexpr int KP = HD + 8;          // K tile pitch (elements)
-  constexpr int VP = kAttnKeys + 4;   // V^T tile pitch (elements)
+  constexpr int VP = kAttnKeys + 8;   // V^T tile pitch (elements; rows 16-byte aligned)
   constexpr int NKC = HD / 32;        // 32-wide hd chunks for S
   constexpr int NCB = HD / 16;        // 16-wide hd blocks for O
   __shared__ __attribute__((aligned(16))) bf16_t sK[kAttnKeys * KP];
@@ -72,32 +74,40 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   }
 
   const size_t slab = ((size_t)b * nkv + g) * N * HD;
-  const bf16_t* kslab = kc + slab;
-  const bf16_t* vslab = vc + slab;
+  const bf16_t* kslab = kc + slab;   // [N][HD]
+  const bf16_t* vslab = vc + slab;   // [HD][N]
   const int key0 = blockIdx.z * keys_per_split;
   const int key1 = min(N, key0 + keys_per_split);
   const float scale = kLog2e / sqrtf((float)HD);
+  const bool vec_v = (N % 8) == 0;   // V^T rows 16-byte aligned
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int CH = kAttnKeys * HD / 8;  // 16-byte chunks per tile
+  constexpr int CH = kAttnKeys * HD / 8;  // 16-byte chunks per tile (K or V^T)
   for (int t0 = key0; t0 < key1; t0 += kAttnKeys) {
     __syncthreads();  // previous tile fully consumed
     for (int c = tid; c < CH; c += 256) {
+      // K tile: 64 keys x HD
       const int kr = c / (HD / 8), cc = (c % (HD / 8)) * 8;
-      const int key = t0 + kr;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (key < key1) {
-        kv = *(const uint4*)(kslab + (size_t)key * HD + cc);
-        vv = *(const uint4*)(vslab + (size_t)key * HD + cc);
-      }
+      uint4 kv = make_uint4(0, 0, 0, 0);
+      if (t0 + kr < key1) kv = *(const uint4*)(kslab + (size_t)(t0 + kr) * HD + cc);
       *(uint4*)&sK[kr * KP + cc] = kv;
-      const bf16_t* ve = (const bf16_t*)&vv;
+      // V^T tile: HD rows x 64 keys
+      const int vr = c / (kAttnKeys / 8), vk = (c % (kAttnKeys / 8)) * 8;
+      const bf16_t* vsrc = vslab + (size_t)vr * N + t0 + vk;
+      uint4 vv = make_uint4(0, 0, 0, 0);
+      if (vec_v && t0 + vk + 8 <= key1) {
+        vv = *(const uint4*)vsrc;
+      } else {
+        bf16_t* ve = (bf16_t*)&vv;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sVt[(cc + j) * VP + kr] = ve[j];
+        for (int j = 0; j < 8; ++j)
+          if (t0 + vk + j < key1) ve[j] = vsrc[j];
+      }
+      *(uint4*)&sVt[vr * VP + vk] = vv;
     }
     __syncthreads();
 
@@ -155,6 +165,204 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 
   if (!qok) return;
   const int gq = row * nq + head;  // global query-vector id
+  if (SPLIT) {
+    const size_t base = (size_t)blockIdx.z * M * nq + gq;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part_o[base * HD + cb * 16 + (lane >> 4) * 4 + i] = oacc[cb][i];
+    if ((lane >> 4) == 0) {
+      part_ml[base * 2] = m_run;
+      part_ml[base * 2 + 1] = l_run;
+    }
+  } else {
+    const float inv = 1.f / l_run;
+    bf16_t* op = o + (size_t)row * nq * HD + (size_t)head * HD;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int c = cb * 16 + (lane >> 4) * 4;
+      ushort4 w;
+      w.x = f2bf(oacc[cb][0] * inv);
+      w.y = f2bf(oacc[cb][1] * inv);
+      w.z = f2bf(oacc[cb][2] * inv);
+      w.w = f2bf(oacc[cb][3] * inv);
+      *(ushort4*)(op + c) = w;
+    }
+  }
+}
+
+// DMA variant (N % 64 == 0): K and V^T tiles go straight from global memory
+// into a STAGES-deep LDS ring with global_load_lds_dwordx4, the next tiles in
+// flight while the current one is consumed.  K tile rows (one key, HD
+// elements) and V^T tile rows (one hd column, 64 keys = 128 B) are stored with
+// their 16-byte chunks XOR-swizzled by the row index so that the fragment
+// reads hit distinct banks.
+typedef __attribute__((address_space(3))) void attn_lds_void;
+__device__ __forceinline__ void attn_dma16(const void* g, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (attn_lds_void*)lds, 16, 0, 0);
+}
+// Slot XORs measured conflict-free on gfx950 (SQ_LDS_BANK_CONFLICT): 16-byte
+// reads of 16 consecutive K rows at one chunk -> r & 15 (256-byte rows) or
+// r & 7 (128-byte rows); 8-byte reads of 16 consecutive V^T rows ->
+// (r & 7) ^ ((r >> 3) & 1).
+__device__ __forceinline__ int kswz(int r, int chunks) { return chunks == 16 ? (r & 15) : (r & 7); }
+__device__ __forceinline__ int vswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+template <int N>
+__device__ __forceinline__ void attn_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int HD, bool SPLIT, int STAGES>
+__global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ row_start,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ o, int N,
+    int nq, int nkv, int keys_per_split, int M, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  constexpr int NKC = HD / 32, NCB = HD / 16;
+  constexpr int KCH = HD / 8;                       // 16-byte chunks per K row
+  constexpr int K_BYTES = kAttnKeys * HD * 2, V_BYTES = HD * kAttnKeys * 2;
+  constexpr int STAGE = K_BYTES + V_BYTES;
+  constexpr int K_INSTR = K_BYTES / 1024, V_INSTR = V_BYTES / 1024;
+  constexpr int IPW = (K_INSTR + V_INSTR) / 4;      // per wave
+  static_assert((K_INSTR + V_INSTR) % 4 == 0, "instructions per wave");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bg = blockIdx.y;
+  const int b = bg / nkv, g = bg % nkv;
+  const int G = nq / nkv;
+  const int r0 = row_start[b], Mb = row_start[b + 1] - r0;
+  const int Qn = Mb * G;
+  const int qbase = blockIdx.x * kAttnQ;
+  if (qbase >= Qn) return;
+
+  const int qv = qbase + wave * 16 + (lane & 15);
+  const bool qok = qv < Qn;
+  const int row = r0 + (qok ? qv / G : 0);
+  const int head = g * G + (qok ? qv % G : 0);
+  bf16x8 qf[NKC];
+  {
+    const bf16_t* qp = q + (size_t)row * nq * HD + (size_t)head * HD + (lane >> 4) * 8;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      if (qok) {
+        qf[c] = *(const bf16x8*)(qp + c * 32);
+      } else {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        qf[c] = *(const bf16x8*)&z;
+      }
+    }
+  }
+  const size_t slab = ((size_t)b * nkv + g) * N * HD;
+  const bf16_t* kslab = kc + slab;  // [N][HD]
+  const bf16_t* vslab = vc + slab;  // [HD][N]
+  const int key0 = blockIdx.z * keys_per_split;
+  const int key1 = min(N, key0 + keys_per_split);
+  const int ntiles = key1 > key0 ? (key1 - key0) / kAttnKeys : 0;
+  const float scale = kLog2e / sqrtf((float)HD);
+
+  // this lane's global source for each of its DMA instructions (tile 0)
+  const bf16_t* src[IPW];
+  int dst[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int j = wave + i * 4;
+    if (j < K_INSTR) {
+      const int kr = j * (1024 / (HD * 2)) + lane / KCH;       // key row in the tile
+      const int lc = (lane % KCH) ^ kswz(kr, KCH);
+      src[i] = kslab + (size_t)(key0 + kr) * HD + lc * 8;
+      dst[i] = j * 1024;
+    } else {
+      const int jv = j - K_INSTR;
+      const int vr = jv * 8 + (lane >> 3);                      // hd row of V^T
+      const int lc = (lane & 7) ^ vswz(vr);
+      src[i] = vslab + (size_t)vr * N + key0 + lc * 8;
+      dst[i] = K_BYTES + jv * 1024;
+    }
+  }
+  auto issue = [&](int t) {
+    unsigned char* st = smem + (t % STAGES) * STAGE;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int j = wave + i * 4;
+      const size_t adv = j < K_INSTR ? (size_t)t * kAttnKeys * HD : (size_t)t * kAttnKeys;
+      attn_dma16(src[i] + adv, st + dst[i]);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < ntiles) issue(t);
+  for (int t = 0; t < ntiles; ++t) {
+    // this wave's loads of tile t (later tiles may stay in flight)
+    const int ahead = min(STAGES - 2, ntiles - 1 - t);
+    if (STAGES >= 4 && ahead >= 2) attn_wait_vmcnt<2 * IPW>();
+    else if (STAGES >= 3 && ahead >= 1) attn_wait_vmcnt<IPW>();
+    else attn_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();   // everyone's loads of t; everyone done with t-1
+    if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1);
+    const unsigned char* st = smem + (t % STAGES) * STAGE;
+    f32x4 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = kb * 16 + (lane & 15);
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+        const int lc = c * 4 + (lane >> 4);
+        const bf16x8 a =
+            *(const bf16x8*)(st + r * (HD * 2) + ((lc ^ kswz(r, KCH)) << 4));
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[kb], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[kb][i] *= scale;
+        mx = fmaxf(mx, s[kb][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);  // m_run = -inf -> 0
+    float psum = 0.f;
+    s16x4 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(s[kb][i] - m_new);
+        psum += p;
+        pb[kb][i] = (short)f2bf(p);
+      }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      oacc[cb] *= alpha;
+      const int vr = cb * 16 + (lane & 15);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int u = kb * 4 + (lane >> 4);  // 8-byte unit: 4 keys
+        const s16x4 va = *(const s16x4*)(st + K_BYTES + vr * 128 +
+                                          (((u >> 1) ^ vswz(vr)) << 4) + ((u & 1) << 3));
+        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kb], oacc[cb], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!qok) return;
+  const int gq = row * nq + head;
   if (SPLIT) {
     const size_t base = (size_t)blockIdx.z * M * nq + gq;
 #pragma unroll
@@ -245,7 +453,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int col = lane + 64 * c;
-      acc[c] = acc[c] * a + (col < hd ? p * ld(vc, slab + (size_t)j * hd + col) : 0.f);
+      acc[c] = acc[c] * a + (col < hd ? p * ld(vc, slab + (size_t)col * N + j) : 0.f);
     }
     m = mn;
   }
@@ -276,8 +484,10 @@ AttnPlan make_attn_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd)
   // estimated busy workgroups: the rows are spread over the sequences
   const int busy = std::max(1, (M * G + kAttnQ - 1) / kAttnQ) * nkv;
   const int ktiles = (N + kAttnKeys - 1) / kAttnKeys;
+  // split the keys only when few workgroups would run (the combine pass
+  // costs a write and a read of every partial output)
   int splits = 1;
-  while (busy * splits < 512 && ktiles / (splits * 2) >= 1 &&
+  while (busy * splits < 128 && ktiles / (splits * 2) >= 2 &&
          (size_t)(splits * 2) * M * nq * (hd + 2) * sizeof(float) <= (64ull << 20))
     splits *= 2;
   p.splits = splits;
@@ -286,26 +496,51 @@ AttnPlan make_attn_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd)
   return p;
 }
 
+template <int HD, bool SPLIT>
+void launch_attn_kernel(dim3 grid, bool dma, const void* q, const int32_t* row_start,
+                        const void* kc, const void* vc, void* o, int N, int nq, int nkv,
+                        int kps, int M, float* po, float* pml, hipStream_t s) {
+  if (dma) {
+    // 4 stages (128 KB of LDS at hd 128, one workgroup per CU) keep three
+    // tiles in flight
+    constexpr int STAGES = HD == 128 ? 4 : 4;
+    constexpr size_t lds = STAGES * (size_t)(2 * kAttnKeys * HD * 2);
+    static bool attr = false;
+    if (!attr) {
+      (void)hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&attn_mfma_dma_kernel<HD, SPLIT, STAGES>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      attr = true;
+    }
+    attn_mfma_dma_kernel<HD, SPLIT, STAGES><<<grid, 256, lds, s>>>(
+        (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq,
+        nkv, kps, M, po, pml);
+  } else {
+    attn_mfma_kernel<HD, SPLIT><<<grid, 256, 0, s>>>((const bf16_t*)q, row_start,
+                                                     (const bf16_t*)kc, (const bf16_t*)vc,
+                                                     (bf16_t*)o, N, nq, nkv, kps, M, po, pml);
+  }
+}
+
 template <int HD>
 hipError_t run_attn_mfma(const AttnPlan& p, int M, int B, int N, int nq, int nkv,
                          const void* q, const int32_t* row_start, const void* kc,
                          const void* vc, void* o, void* ws, hipStream_t s) {
   dim3 grid(p.qtiles, B * nkv, p.splits);
+  const bool dma = (N % kAttnKeys) == 0;
   if (p.splits > 1) {
     float* po = (float*)ws;
     float* pml = po + (size_t)p.splits * M * nq * HD;
-    attn_mfma_kernel<HD, true><<<grid, 256, 0, s>>>(
-        (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq,
-        nkv, p.keys_per_split, M, po, pml);
+    launch_attn_kernel<HD, true>(grid, dma, q, row_start, kc, vc, o, N, nq, nkv,
+                                 p.keys_per_split, M, po, pml, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t total = (size_t)M * nq * HD;
     const int gsz = (int)std::min<size_t>((total + 255) / 256, 8192);
     attn_combine_kernel<bf16_t><<<gsz, 256, 0, s>>>(po, pml, p.splits, M * nq, HD, (bf16_t*)o);
   } else {
-    attn_mfma_kernel<HD, false><<<grid, 256, 0, s>>>(
-        (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq,
-        nkv, p.keys_per_split, M, nullptr, nullptr);
+    launch_attn_kernel<HD, false>(grid, dma, q, row_start, kc, vc, o, N, nq, nkv,
+                                  p.keys_per_split, M, nullptr, nullptr, s);
   }
   return hipGetLastError();
 }

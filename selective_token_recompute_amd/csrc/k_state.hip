@@ -42,6 +42,7 @@ hipError_t launch_init_state(int B, int N, int P, int mask_id, const int32_t* pr
 }
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
 // Compaction: one workgroup of 1024 threads scans the B*N positions in
 // (seq, pos) order, 1024 at a time.  Each wave ballots its 64 "active"
 // predicates; the lane's rank is the popcount of the ballot below it, the

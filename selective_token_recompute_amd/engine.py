@@ -239,10 +239,12 @@ class Engine:
                           (self.run.batch, self.run.seq_len, self.shape.vocab))
 
     def kv_cache(self):
+        """K [L][B][nkv][N][hd] and V transposed [L][B][nkv][hd][N]."""
         sh = (self.shape.n_layers, self.run.batch, self.shape.n_kv_heads, self.run.seq_len,
               self.shape.head_dim)
+        sht = sh[:3] + (sh[4], sh[3])
         dt = torch.bfloat16 if self.shape.bf16 else torch.float32
-        return self._view(L.DLM_GET_KCACHE, dt, sh), self._view(L.DLM_GET_VCACHE, dt, sh)
+        return self._view(L.DLM_GET_KCACHE, dt, sh), self._view(L.DLM_GET_VCACHE, dt, sht)
 
     def last_step_info(self):
         s = ctypes.c_int32()

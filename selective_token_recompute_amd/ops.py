@@ -75,11 +75,43 @@ def gemm(epi: int, A: torch.Tensor, W: torch.Tensor, W2=None, C=None, row_seq=No
             raise ValueError("C required for this epilogue")
     need = gemm_ws_bytes(dt, epi, M, N, K)
     if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=A.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=A.device)  # split counters start at 0
     L.check(L.lib().dlm_op_gemm(dt, epi, M, N, K, _p(A), _p(W), _p(W2), _p(C), _p(row_seq),
                                 _p(row_pos), seq_len, mask_id, _p(ws),
                                 0 if ws is None else ws.numel(), _s()), "dlm_op_gemm")
     return C
+
+
+def gemm_config(epi: int, A, W, cfg: int, splits: int = 0, W2=None, C=None, row_seq=None,
+                row_pos=None, seq_len: int = 0, mask_id: int = 0):
+    """GEMM with a forced tile configuration (cfg) and split-K factor."""
+    M, K = A.shape
+    N = W.shape[0]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32 if epi != L.DLM_EPI_SWIGLU else A.dtype,
+                        device=A.device)
+    need = max(splits, 1) * M * N * (8 if epi == L.DLM_EPI_SWIGLU else 4)
+    ws = _ws_cache(need, A.device)
+    L.check(L.lib().dlm_op_gemm_config(_dt(A), epi, M, N, K, _p(A), _p(W), _p(W2), _p(C),
+                                       _p(row_seq), _p(row_pos), seq_len, mask_id, cfg, splits,
+                                       _p(ws), ws.numel(), _s()), "dlm_op_gemm_config")
+    return C
+
+
+_WS = {}
+
+
+def _ws_cache(nbytes, device):
+    """A zeroed workspace reused across calls (split counters are left zero)."""
+    t = _WS.get(device)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _WS[device] = t
+    return t
+
+
+def num_gemm_configs() -> int:
+    return int(L.lib().dlm_op_gemm_num_configs())
 
 
 def rope_table(seq_len: int, head_dim: int, base: float, device="cuda") -> torch.Tensor:

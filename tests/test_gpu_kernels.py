@@ -155,8 +155,9 @@ def _attn_case(B, N, nq, nkv, hd, rows_per_seq, seed, bf16=True):
 ])
 def test_attention_bf16_mfma(B, N, nq, nkv, hd, rows):
     q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, rows, seed=N + nq)
+    # the engine caches V transposed: [B][nkv][hd][N]
     o = ops.attention(_dev(q.reshape(len(rs), nq * hd)), torch.from_numpy(rst).to(DEV),
-                      _dev(kc), _dev(vc), nq, nkv, hd)
+                      _dev(kc), _dev(vc.transpose(0, 1, 3, 2)), nq, nkv, hd)
     ref = oracle.unit_attention(q, rs, kc, vc).reshape(len(rs), nq * hd)
     err = np.abs(_f64(o) - ref)
     # P is rounded to bf16 before the PV product and o is stored in bf16
@@ -168,7 +169,7 @@ def test_attention_fp32_generic():
     q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, [20, 7], seed=3, bf16=False)
     o = ops.attention(_dev(q.reshape(len(rs), nq * hd), torch.float32),
                       torch.from_numpy(rst).to(DEV), _dev(kc, torch.float32),
-                      _dev(vc, torch.float32), nq, nkv, hd)
+                      _dev(vc.transpose(0, 1, 3, 2), torch.float32), nq, nkv, hd)
     ref = oracle.unit_attention(q, rs, kc, vc).reshape(len(rs), nq * hd)
     assert np.abs(_f64(o) - ref).max() <= 1e-5
 
@@ -360,7 +361,7 @@ def test_rope_scatter(bf16):
     table = ops.rope_table(N, hd, 10000.0)
     q = torch.zeros((M, nq * hd), dtype=dt, device=DEV)
     kc = torch.full((B, nkv, N, hd), 3.0, dtype=dt, device=DEV)
-    vc = torch.full((B, nkv, N, hd), 3.0, dtype=dt, device=DEV)
+    vc = torch.full((B, nkv, hd, N), 3.0, dtype=dt, device=DEV)  # transposed V cache
     ops.rope_scatter(torch.from_numpy(qkv).to(DEV), torch.from_numpy(rs).to(DEV),
                      torch.from_numpy(rp).to(DEV), table, q, kc, vc, nq, nkv, hd)
     x = qkv.astype(np.float64).reshape(M, nq + 2 * nkv, hd)
@@ -373,7 +374,50 @@ def test_rope_scatter(bf16):
         kr = rot[i, nq:]
         assert (np.abs(kcn[rs[i], :, rp[i]] - kr) <= tol(kr)).all()
         vr = x[i, nq + nkv:]
-        assert (np.abs(vcn[rs[i], :, rp[i]] - vr) <= tol(vr)).all()
+        assert (np.abs(vcn[rs[i], :, :, rp[i]] - vr) <= tol(vr)).all()
     touched = np.zeros((B, N), bool)
     touched[rs, rp] = True
-    assert (kcn[:, :, :][np.broadcast_to(~touched[:, None, :], kcn.shape[:3])] == 3.0).all()
+    assert (kcn[np.broadcast_to(~touched[:, None, :], kcn.shape[:3])] == 3.0).all()
+    assert (np.moveaxis(vcn, 3, 2)[np.broadcast_to(~touched[:, None, :], kcn.shape[:3])] == 3.0).all()
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("epi", [L.DLM_EPI_STORE_F32, L.DLM_EPI_RESID_ADD, L.DLM_EPI_SWIGLU,
+                                 L.DLM_EPI_LOGITS])
+def test_gemm_every_tile_config(epi, splits):
+    """Every MFMA tile configuration the plan may choose, with and without
+    split-K (the last workgroup of a tile reduces), called twice on the same
+    workspace, against the oracle; ragged M and N exercise the guards."""
+    M, N, K = 77, 200, 384
+    A, W, W2 = _gemm_inputs(M, N, K, seed=31)
+    g = oracle.unit_linear(A, W)
+    if epi == L.DLM_EPI_SWIGLU:
+        u = oracle.unit_linear(A, W2)
+        ref = g / (1 + np.exp(-g)) * u
+    else:
+        ref = g
+    rs = torch.zeros(M, dtype=torch.int32, device=DEV)
+    rp = torch.arange(M, dtype=torch.int32, device=DEV)
+    for cfg in range(ops.num_gemm_configs()):
+        if epi == L.DLM_EPI_SWIGLU and cfg == 7:
+            continue  # 16-column wave tiles cannot pair gate and up columns
+        for call in range(2):
+            if epi == L.DLM_EPI_RESID_ADD:
+                h0 = synth.gen_normal((M, N), 5 + call, 1.0)
+                C = torch.from_numpy(h0).to(DEV)
+                ops.gemm_config(epi, _dev(A), _dev(W), cfg, splits, C=C)
+                got, want = _f64(C), h0.astype(np.float64) + ref
+            elif epi == L.DLM_EPI_LOGITS:
+                C = torch.zeros((1, 96, N), device=DEV)
+                ops.gemm_config(epi, _dev(A), _dev(W), cfg, splits, C=C, row_seq=rs, row_pos=rp,
+                                seq_len=96, mask_id=N - 1)
+                got = C.cpu().numpy()[0, :M].astype(np.float64)
+                assert np.isneginf(got[:, N - 1]).all()
+                got, want = got[:, :-1], ref[:, :-1]
+            else:
+                C = ops.gemm_config(epi, _dev(A), _dev(W), cfg, splits,
+                                    W2=_dev(W2) if epi == L.DLM_EPI_SWIGLU else None)
+                got, want = _f64(C), ref
+            tol = (2.0 ** -8 * np.abs(want) + 1e-5) if epi == L.DLM_EPI_SWIGLU else \
+                (2e-5 * max(1.0, np.abs(want).max()))
+            assert (np.abs(got - want) <= tol).all(), (cfg, call, np.abs(got - want).max())

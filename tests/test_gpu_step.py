@@ -185,3 +185,43 @@ def test_override_path_matches_oracle(tiny):
         assert np.array_equal(lk, bool_to_bits(orc.locked()))
         assert np.array_equal(eng.counters().cpu().numpy(), orc.counters())
     eng.close()
+
+
+@pytest.mark.parametrize("shape", [MID, MID_GQA], ids=["mha", "gqa"])
+def test_kv_cache_matches_oracle(shape):
+    """The per-layer K cache and the transposed V cache written by the fused
+    QKV epilogue (M >= 96) and by the unfused rotary/scatter path (small M)
+    equal the oracle's caches within bf16 rounding."""
+    run = MID_RUN
+    W = synth.gen_weights(shape)
+    pr = synth.gen_prompts(shape, run)
+    dev = torch.device("cuda")
+    lock = synth.LOCK_SETTINGS["scheduled"]
+    eng = E.Engine(shape, E.upload_weights(W, shape, dev), run, lock, torch.from_numpy(pr).to(dev))
+    orc = oracle.Oracle(shape, W, run, lock, pr)
+    ms = []
+    for t in range(run.steps):
+        ms.append(eng.step())
+        orc.step()
+        if t in (0, run.steps - 1):
+            kg, vg = eng.kv_cache()
+            for layer in range(shape.n_layers):
+                ko, vo = orc.kv(layer)
+                kgl = kg[layer].float().cpu().numpy()
+                vgl = vg[layer].float().cpu().numpy().transpose(0, 1, 3, 2)
+                for got, want in ((kgl, ko), (vgl, vo)):
+                    err = np.abs(got - want)
+                    scale = float(np.abs(want).max())
+                    # layer 0 sees identical inputs: one bf16 rounding apart; deeper
+                    # layers inherit fp32-vs-fp64 differences, so a 1% scale bar
+                    tol = (2.0 ** -7 * np.abs(want) + 1e-3 * scale) if layer == 0 else \
+                        1e-2 * scale
+                    assert (err <= tol).all(), (t, layer, err.max(), scale)
+        orc.lock_update()
+        # follow the oracle's decisions so both caches see the same inputs
+        from tests.harness import bool_to_bits
+        cs, cp, ct = orc.commits()
+        eng.lock_update(commits=(cs, cp, ct), lock_bits=bool_to_bits(orc.locked()),
+                        counters=orc.counters())
+    assert max(ms) >= 96 and min(ms) < 96  # both QKV paths ran
+    eng.close()
