@@ -52,19 +52,21 @@ __device__ __forceinline__ void epi_store(const EpiParams& p, int row, int col, 
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel.
-//   Tile BM x BN x 64, WAVES_M x WAVES_N waves, each wave (BM/WAVES_M) x
-//   (BN/WAVES_N) made of 16x16 MFMA tiles.  For SwiGLU (DUAL) the BN tile
-//   rows are [BN/2 gate rows | BN/2 up rows] of the same BN/2 features, and
-//   each wave owns matching gate/up column tiles so the epilogue pairs them
-//   in registers.
+//   Tile BM x BN, K consumed in slices of BK (32 or 64), WAVES_M x WAVES_N
+//   waves, each wave (BM/WAVES_M) x (BN/WAVES_N) made of 16x16 MFMA tiles.
+//   For SwiGLU (DUAL) the BN tile rows are [BN/2 gate rows | BN/2 up rows]
+//   of the same BN/2 features, and each wave owns matching gate/up column
+//   tiles so the epilogue pairs them in registers.
 //   Operands go straight from global memory into an LDS ring of STAGES
-//   stages with global_load_lds_dwordx4: one wave instruction fills 1 KB =
-//   8 tile rows of 128 B; lane i writes row i/8, 16-byte slot i%8, and loads
-//   the global chunk slot ^ (row & 7), so that the fragment reads below are
-//   free of bank conflicts.  The loads of stage kt+STAGES-1 are issued before stage kt is
-//   consumed; an explicit vmcnt wait (counting this wave's instructions of
-//   the later stages still in flight) plus a workgroup barrier publish a
-//   stage.
+//   k-slices with global_load_lds_dwordx4: one wave instruction fills 1 KB
+//   of consecutive tile rows of 2 BK bytes; lane i writes row i/CH, 16-byte
+//   slot i%CH (CH = BK/8 slots per row) and loads the global chunk
+//   slot ^ x(row), where x is the slot XOR that keeps the fragment reads
+//   below free of bank conflicts.  Slices kt+1 .. kt+STAGES-1 are in flight
+//   while slice kt is multiplied; an explicit vmcnt wait (counting this
+//   wave's load instructions of the later slices) plus a workgroup barrier
+//   publish a slice, and the slot of slice kt-1 is refilled right after that
+//   barrier (every wave has finished slice kt-1 by then).
 //   v_mfma_f32_16x16x32_bf16: lane l supplies A[row l%16][k-group l/16] and
 //   B[k-group l/16][col l%16] (8 consecutive k each; the same k mapping on
 //   both sides) and receives C[4*(l/16)+i][l%16], i = 0..3.
@@ -72,11 +74,15 @@ __device__ __forceinline__ void epi_store(const EpiParams& p, int row, int col, 
 //   the epilogue, NC = N (2N for DUAL: gate at f, up at N+f).
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16-byte slot XOR for 128-byte tile rows.  Measured on gfx950 with
-// SQ_LDS_BANK_CONFLICT: the fragment reads below (lane l: row l%16, chunk
-// l/16) are conflict-free with r & 7 and two-way conflicted with padded rows
-// or with (r & 7) ^ ((r >> 3) & 1).
-__device__ __forceinline__ int swz(int r) { return r & 7; }
+// 16-byte slot XOR by tile row, measured conflict-free on gfx950
+// (SQ_LDS_BANK_CONFLICT) for the fragment reads (lane l: row l%16, slot l/16):
+// 128-byte rows (8 slots): r & 7; 64-byte rows (4 slots): (r >> 1) & 2.  (For
+// 64-byte rows, (r >> 2) & 3 is two-way conflicted.)
+template <int CH>
+__device__ __forceinline__ int slot_xor(int r) {
+  if constexpr (CH == 8) return r & 7;
+  else return (r >> 1) & 2;
+}
 
 // One 16-byte-per-lane direct load from global memory into LDS; the LDS
 // destination (wave-uniform) receives lane i's 16 bytes at offset 16 i.
@@ -93,22 +99,67 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int EPI, bool SPLIT>
+// Waits until at most n (0 <= n < S) k-slices of IPW load instructions each
+// are still in flight for this wave.
+template <int IPW, int S>
+__device__ __forceinline__ void wait_slices(int n) {
+  if constexpr (S <= 1) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= S - 1) wait_vmcnt<(S - 1) * IPW>();
+    else wait_slices<IPW, S - 1>(n);
+  }
+}
+
+// Workgroup barrier without the vmcnt(0) that __syncthreads() implies; the
+// empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <typename T>
+__device__ __forceinline__ T sel4(const T (&a)[4], int i) {
+  return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
+}
+
+// One round of a 4x4 transpose within lane quads: lane t sends pk[(t+K)&3],
+// and the value received from lane (t-K)&3 (DPP quad_perm CTRL) is that
+// lane's column for row t, stored at T[(t-K)&3].  Before the first round
+// T[t] = pk[t]; after rounds 1..3, T[s] = (row t, column 4*(quad)+s).
+template <int K, int CTRL>
+__device__ __forceinline__ void quad_round(const unsigned (&pk)[4], unsigned (&T)[4], int t) {
+  const unsigned send = sel4(pk, (t + K) & 3);
+  const unsigned recv =
+      (unsigned)__builtin_amdgcn_update_dpp(0, (int)send, CTRL, 0xf, 0xf, false);
+  const int s = (t - K) & 3;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) T[q] = (q == s) ? recv : T[q];
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, const bf16_t* __restrict__ W2,
     EpiParams ep, int K, int k_per_split, int tiles_m, int tiles_n, float* __restrict__ partial) {
   constexpr bool DUAL = EPI == kEpiSwiglu;
-  constexpr int BK = 64;
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int ROWS = BM + BN;                // tile rows per stage (A then B)
-  constexpr int INSTR = ROWS / 8;              // 1 KB load instructions per stage
+  constexpr int KS = BK / 32;                  // MFMA k-steps per slice
+  constexpr int CH = BK / 8;                   // 16-byte slots per tile row
+  constexpr int RB = BK * 2;                   // bytes per tile row
+  constexpr int RPI = 64 / CH;                 // tile rows per 1 KB load instruction
+  constexpr int ROWS = BM + BN;                // tile rows per slice (A then B)
+  constexpr int INSTR = ROWS / RPI;            // load instructions per slice
   constexpr int IPW = INSTR / NW;              // per wave
-  constexpr int STAGE_BYTES = ROWS * 128;
-  static_assert(INSTR % NW == 0, "load instructions must split evenly over the waves");
+  constexpr int STAGE_BYTES = ROWS * RB;
+  static_assert(BK == 32 || BK == 64, "k-slice");
+  static_assert(ROWS % RPI == 0 && INSTR % NW == 0,
+                "load instructions must split evenly over the waves");
+  static_assert((STAGES - 1) * IPW < 64, "in-flight loads must fit the vmcnt counter");
   static_assert(!DUAL || (TN % 2 == 0), "dual tiles need an even number of column tiles");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(STAGES >= 2 && STAGES <= 8, "stages");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -132,9 +183,9 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
   const bf16_t* src[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int j = wave + i * NW;             // instruction index within the stage
-    const int r = j * 8 + (lane >> 3);       // tile row (A rows then B rows)
-    const int chunk = (lane & 7) ^ swz(r);   // global 16-byte chunk for slot lane&7
+    const int j = wave + i * NW;                   // instruction index within the slice
+    const int r = j * RPI + lane / CH;             // tile row (A rows then B rows)
+    const int chunk = (lane % CH) ^ slot_xor<CH>(r);  // global chunk for this slot
     const bf16_t* base;
     if (r < BM) {
       const int gr = min(m0 + r, M - 1);     // rows past M load a valid row; discarded
@@ -178,44 +229,48 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s);
-
+  struct Frags {
+    bf16x8 a[KS][TM], b[KS][TN];
+  };
   const int lr = lane & 15, lk = lane >> 4;
-  for (int kt = 0; kt < KT; ++kt) {
-    // wait for this wave's loads of stage kt (the later stages issued so far
-    // may stay in flight), then publish the stage to the workgroup
-    const int ahead = min(STAGES - 2, KT - 1 - kt);
-    if (STAGES >= 4 && ahead >= 2) wait_vmcnt<2 * IPW>();
-    else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<IPW>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    // every wave has finished iteration kt-1, so its stage can be refilled
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-    const unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    bf16x8 af[BK / 32][TM], bfr[BK / 32][TN];
+  auto read_frags = [&](int slice, Frags& F) {
+    const unsigned char* st = smem + (slice % STAGES) * STAGE_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * WM + i * 16 + lr;
-        af[ks][i] = *(const bf16x8*)(st + r * 128 + (((ks * 4 + lk) ^ swz(r)) << 4));
+        F.a[ks][i] = *(const bf16x8*)(st + r * RB + (((ks * 4 + lk) ^ slot_xor<CH>(r)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int r = BM + brow(j) + lr;
-        bfr[ks][j] = *(const bf16x8*)(st + r * 128 + (((ks * 4 + lk) ^ swz(r)) << 4));
+        F.b[ks][j] = *(const bf16x8*)(st + r * RB + (((ks * 4 + lk) ^ slot_xor<CH>(r)) << 4));
       }
     }
+  };
+  auto mma = [&](const Frags& F) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(F.a[ks][i], F.b[ks][j], acc[i][j], 0, 0, 0);
+  };
+  // slice kt: publish it, refill the slot of slice kt-1 (every wave has
+  // passed this barrier, so it finished slice kt-1), then read and multiply
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_slices<IPW, STAGES - 1>(min(STAGES - 2, KT - 1 - kt));
+    lds_barrier();
+    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+    Frags f;
+    read_frags(kt, f);
+    mma(f);
   }
 
   // epilogue
@@ -250,20 +305,43 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
             cs[jt][qq] = t2.x;
             sn[jt][qq] = t2.y;
           }
+        // 4x4 transpose inside each quad of lanes (DPP quad permutes) so that
+        // lane t of a quad holds row rq+t at 4 consecutive columns: one
+        // 8-byte store per half-head instead of four 2-byte stores
+        const int t = cl & 3, c4 = cl & ~3;
+        const int row_t = sel4(rows, t);
+        bf16_t* dst = hix < nq ? ep.q + (size_t)row_t * nq * 128 + (size_t)hix * 128
+                               : ep.kc + (((size_t)sel4(seqs, t) * nkv + (hix - nq)) * Nseq +
+                                          sel4(poss, t)) * 128;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-          const int c = jt * 16 + cl;  // rotary pair (c, c + 64)
+          // rotary pair (c, c + 64), c = jt * 16 + cl; low half c, high half c + 64
+          unsigned pk[4];
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
-            if (rows[qq] >= M) continue;
             const float a0 = acc[i][jt][qq], a1 = acc[i][jt + 4][qq];
             const float r0 = a0 * cs[jt][qq] - a1 * sn[jt][qq];
             const float r1 = a0 * sn[jt][qq] + a1 * cs[jt][qq];
-            bf16_t* dst = hix < nq
-                              ? ep.q + (size_t)rows[qq] * nq * 128 + (size_t)hix * 128
-                              : ep.kc + (((size_t)seqs[qq] * nkv + (hix - nq)) * Nseq + poss[qq]) * 128;
-            dst[c] = f2bf(r0);
-            dst[c + 64] = f2bf(r1);
+            pk[qq] = (unsigned)f2bf(r0) | ((unsigned)f2bf(r1) << 16);
+          }
+          unsigned T[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) T[q] = pk[q];  // T[t] = pk[t] is the k = 0 round
+          quad_round<1, 0x93>(pk, T, t);
+          quad_round<2, 0x4e>(pk, T, t);
+          quad_round<3, 0x39>(pk, T, t);
+          if (row_t < M) {
+            ushort4 lo, hi;
+            lo.x = (unsigned short)(T[0] & 0xffff);
+            lo.y = (unsigned short)(T[1] & 0xffff);
+            lo.z = (unsigned short)(T[2] & 0xffff);
+            lo.w = (unsigned short)(T[3] & 0xffff);
+            hi.x = (unsigned short)(T[0] >> 16);
+            hi.y = (unsigned short)(T[1] >> 16);
+            hi.z = (unsigned short)(T[2] >> 16);
+            hi.w = (unsigned short)(T[3] >> 16);
+            *(ushort4*)(dst + jt * 16 + c4) = lo;
+            *(ushort4*)(dst + 64 + jt * 16 + c4) = hi;
           }
         }
       } else {
@@ -422,41 +500,46 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(const T* __restrict__
 // ---------------------------------------------------------------------------
 // Launch plans.
 //
-// Tile configurations (rows x cols, waves, LDS stages).  The plan picks the
-// configuration by M (the ragged active-row count) and splits K while the
-// grid would leave CUs idle.
+// Tile configurations (rows x cols, waves, k-slices in the LDS ring, k-slice
+// width).  The plan picks the configuration by M (the ragged active-row
+// count) and splits K while the grid would leave CUs idle.
 namespace {
 
 struct TileCfg {
-  int bm, bn, wm, wn, stages;
+  int bm, bn, wm, wn, stages, bk;
 };
 constexpr TileCfg kCfgs[] = {
-    {32, 128, 1, 4, 4},   // 0: weight streaming
-    {64, 128, 2, 2, 4},   // 1: weight streaming
-    {128, 128, 2, 2, 3},  // 2
-    {128, 256, 2, 2, 3},  // 3
-    {256, 128, 2, 2, 3},  // 4
-    {192, 128, 2, 2, 3},  // 5
-    {96, 128, 1, 4, 3},   // 6
-    {32, 64, 1, 4, 4},    // 7: narrow column tiles (not for SwiGLU)
-    {128, 128, 2, 4, 3},  // 8: 8 waves
-    {256, 128, 4, 2, 3},  // 9: 8 waves
-    {128, 256, 2, 4, 3},  // 10: 8 waves
-    {128, 128, 2, 2, 2},  // 11: two workgroups per CU
-    {192, 128, 2, 2, 2},  // 12: two workgroups per CU
-    {256, 256, 2, 4, 2},  // 13: 8 waves, 128x64 per wave
-    {64, 64, 2, 2, 4},    // 14
-    {192, 128, 4, 1, 2},  // 15: one head per wave (fused QKV epilogue)
-    {128, 128, 4, 1, 3},  // 16: one head per wave
-    {256, 128, 4, 1, 2},  // 17: one head per wave
-    {64, 128, 4, 1, 4},   // 18: one head per wave
+    {32, 128, 1, 4, 4, 64},   // 0: weight streaming
+    {64, 128, 2, 2, 4, 64},   // 1: weight streaming
+    {128, 128, 2, 2, 3, 64},  // 2
+    {128, 256, 2, 2, 3, 64},  // 3
+    {256, 128, 2, 2, 3, 64},  // 4
+    {192, 128, 2, 2, 3, 64},  // 5
+    {96, 128, 1, 4, 3, 64},   // 6
+    {32, 64, 1, 4, 4, 64},    // 7: narrow column tiles (not for SwiGLU)
+    {128, 128, 2, 4, 3, 64},  // 8: 8 waves
+    {256, 128, 4, 2, 3, 64},  // 9: 8 waves
+    {128, 256, 2, 4, 3, 64},  // 10: 8 waves
+    {128, 128, 2, 2, 2, 64},  // 11: two workgroups per CU
+    {192, 128, 2, 2, 2, 64},  // 12: two workgroups per CU
+    {256, 256, 2, 4, 2, 64},  // 13: 8 waves, 128x64 per wave
+    {64, 64, 2, 2, 4, 64},    // 14
+    {192, 128, 4, 1, 2, 64},  // 15: one head per wave (fused QKV epilogue)
+    {128, 128, 4, 1, 3, 64},  // 16: one head per wave
+    {256, 128, 4, 1, 2, 64},  // 17: one head per wave
+    {64, 128, 4, 1, 4, 64},   // 18: one head per wave
+    {64, 128, 2, 2, 8, 32},   // 19: weight streaming, 7 slices in flight
+    {64, 64, 2, 2, 8, 32},    // 20: weight streaming, 7 slices in flight
+    {64, 128, 4, 1, 8, 32},   // 21: one head per wave, 7 slices in flight
+    {384, 128, 4, 2, 5, 32},  // 22: 8 waves
+    {192, 128, 2, 2, 4, 64},  // 23
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
-constexpr int kBK = 64;
+constexpr int kBK = 64;  // K granularity every configuration accepts
 constexpr size_t kSplitCapBytes = 64ull << 20;  // split-K partials never exceed this
 constexpr int kCUs = 256;
 
-inline size_t cfg_lds(const TileCfg& c) { return (size_t)c.stages * (c.bm + c.bn) * 128; }
+inline size_t cfg_lds(const TileCfg& c) { return (size_t)c.stages * (c.bm + c.bn) * c.bk * 2; }
 
 struct Plan {
   bool mfma;
@@ -516,7 +599,7 @@ Plan make_plan(int dtype, int epi, int M, int N, int K) {
   return make_plan_cfg(dtype, epi, M, N, K, pick_cfg(M, N, epi == kEpiSwiglu));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI>
 hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hipStream_t s) {
   constexpr bool DUAL = EPI == kEpiSwiglu;
   if constexpr (DUAL && ((BN / WAVES_N / 16) % 2 != 0)) {
@@ -526,18 +609,18 @@ hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hi
   } else {
     dim3 grid(p.tiles_m * p.tiles_n, p.splits, 1);
     const int threads = 64 * WAVES_M * WAVES_N;
-    const size_t lds = (size_t)STAGES * (BM + BN) * 128;
+    const size_t lds = (size_t)STAGES * (BM + BN) * BK * 2;
     float* partial = (float*)ws;
     if (p.splits > 1) {
       static bool attr = false;
       if (!attr) {
         (void)hipFuncSetAttribute(
             reinterpret_cast<const void*>(
-                &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, EPI, true>),
+                &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         attr = true;
       }
-      gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, EPI, true>
+      gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true>
           <<<grid, threads, lds, s>>>((const bf16_t*)a.A, (const bf16_t*)a.W,
                                       (const bf16_t*)a.W2, ep, a.K, p.k_per_split, p.tiles_m,
                                       p.tiles_n, partial);
@@ -551,11 +634,11 @@ hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hi
       if (!attr) {
         (void)hipFuncSetAttribute(
             reinterpret_cast<const void*>(
-                &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, EPI, false>),
+                &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, false>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         attr = true;
       }
-      gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, EPI, false>
+      gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, false>
           <<<grid, threads, lds, s>>>((const bf16_t*)a.A, (const bf16_t*)a.W,
                                       (const bf16_t*)a.W2, ep, a.K, p.k_per_split, p.tiles_m,
                                       p.tiles_n, nullptr);
@@ -568,25 +651,30 @@ template <int EPI>
 hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws,
                          hipStream_t s) {
   switch (p.cfg) {
-    case 0: return run_mfma<32, 128, 1, 4, 4, EPI>(a, p, ep, ws, s);
-    case 1: return run_mfma<64, 128, 2, 2, 4, EPI>(a, p, ep, ws, s);
-    case 2: return run_mfma<128, 128, 2, 2, 3, EPI>(a, p, ep, ws, s);
-    case 3: return run_mfma<128, 256, 2, 2, 3, EPI>(a, p, ep, ws, s);
-    case 4: return run_mfma<256, 128, 2, 2, 3, EPI>(a, p, ep, ws, s);
-    case 5: return run_mfma<192, 128, 2, 2, 3, EPI>(a, p, ep, ws, s);
-    case 6: return run_mfma<96, 128, 1, 4, 3, EPI>(a, p, ep, ws, s);
-    case 7: return run_mfma<32, 64, 1, 4, 4, EPI>(a, p, ep, ws, s);
-    case 8: return run_mfma<128, 128, 2, 4, 3, EPI>(a, p, ep, ws, s);
-    case 9: return run_mfma<256, 128, 4, 2, 3, EPI>(a, p, ep, ws, s);
-    case 10: return run_mfma<128, 256, 2, 4, 3, EPI>(a, p, ep, ws, s);
-    case 11: return run_mfma<128, 128, 2, 2, 2, EPI>(a, p, ep, ws, s);
-    case 12: return run_mfma<192, 128, 2, 2, 2, EPI>(a, p, ep, ws, s);
-    case 13: return run_mfma<256, 256, 2, 4, 2, EPI>(a, p, ep, ws, s);
-    case 14: return run_mfma<64, 64, 2, 2, 4, EPI>(a, p, ep, ws, s);
-    case 15: return run_mfma<192, 128, 4, 1, 2, EPI>(a, p, ep, ws, s);
-    case 16: return run_mfma<128, 128, 4, 1, 3, EPI>(a, p, ep, ws, s);
-    case 17: return run_mfma<256, 128, 4, 1, 2, EPI>(a, p, ep, ws, s);
-    default: return run_mfma<64, 128, 4, 1, 4, EPI>(a, p, ep, ws, s);
+    case 0: return run_mfma<32, 128, 1, 4, 4, 64, EPI>(a, p, ep, ws, s);
+    case 1: return run_mfma<64, 128, 2, 2, 4, 64, EPI>(a, p, ep, ws, s);
+    case 2: return run_mfma<128, 128, 2, 2, 3, 64, EPI>(a, p, ep, ws, s);
+    case 3: return run_mfma<128, 256, 2, 2, 3, 64, EPI>(a, p, ep, ws, s);
+    case 4: return run_mfma<256, 128, 2, 2, 3, 64, EPI>(a, p, ep, ws, s);
+    case 5: return run_mfma<192, 128, 2, 2, 3, 64, EPI>(a, p, ep, ws, s);
+    case 6: return run_mfma<96, 128, 1, 4, 3, 64, EPI>(a, p, ep, ws, s);
+    case 7: return run_mfma<32, 64, 1, 4, 4, 64, EPI>(a, p, ep, ws, s);
+    case 8: return run_mfma<128, 128, 2, 4, 3, 64, EPI>(a, p, ep, ws, s);
+    case 9: return run_mfma<256, 128, 4, 2, 3, 64, EPI>(a, p, ep, ws, s);
+    case 10: return run_mfma<128, 256, 2, 4, 3, 64, EPI>(a, p, ep, ws, s);
+    case 11: return run_mfma<128, 128, 2, 2, 2, 64, EPI>(a, p, ep, ws, s);
+    case 12: return run_mfma<192, 128, 2, 2, 2, 64, EPI>(a, p, ep, ws, s);
+    case 13: return run_mfma<256, 256, 2, 4, 2, 64, EPI>(a, p, ep, ws, s);
+    case 14: return run_mfma<64, 64, 2, 2, 4, 64, EPI>(a, p, ep, ws, s);
+    case 15: return run_mfma<192, 128, 4, 1, 2, 64, EPI>(a, p, ep, ws, s);
+    case 16: return run_mfma<128, 128, 4, 1, 3, 64, EPI>(a, p, ep, ws, s);
+    case 17: return run_mfma<256, 128, 4, 1, 2, 64, EPI>(a, p, ep, ws, s);
+    case 18: return run_mfma<64, 128, 4, 1, 4, 64, EPI>(a, p, ep, ws, s);
+    case 19: return run_mfma<64, 128, 2, 2, 8, 32, EPI>(a, p, ep, ws, s);
+    case 20: return run_mfma<64, 64, 2, 2, 8, 32, EPI>(a, p, ep, ws, s);
+    case 21: return run_mfma<64, 128, 4, 1, 8, 32, EPI>(a, p, ep, ws, s);
+    case 22: return run_mfma<384, 128, 4, 2, 5, 32, EPI>(a, p, ep, ws, s);
+    default: return run_mfma<192, 128, 2, 2, 4, 64, EPI>(a, p, ep, ws, s);
   }
 }
 
