@@ -134,6 +134,99 @@ def cpu_baseline(shape, run):
                 sample_seconds=round(t_all, 2))
 
 
+GEMM_CLASSES = ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down")
+
+
+def layer_isolation(n_caches=32, launches=100, warmup=10):
+    """One bf16 layer at LLaDA-8B width over an N=1024 cache, at M = 1024,
+    512, 256, 102 and 20 active rows (a sorted uniform random subset, seed
+    2).  Runs through the engine with a one-layer model and a 256-entry
+    vocabulary (so the LM head and statistics are negligible and not
+    reported); n_caches engines with their own cache (K, V ~ N(0, 1) bf16)
+    are stepped round-robin so the 16.8 MB caches (537 MB in all) and the
+    436 MB of layer weights are not served from the 256 MB Infinity Cache.
+    Per-kernel times come from the engine's HIP events."""
+    import dataclasses
+    import numpy as np
+    import torch
+    import synth
+    from selective_token_recompute_amd import engine as E
+
+    cfg = synth.LAYER_ISOLATION
+    shape = dataclasses.replace(cfg["shape"], vocab=256)
+    N = cfg["cache_len"]
+    run = synth.RunShape(1, N, N // 2, 4 * launches, N // 2)
+    lock = synth.LOCK_SETTINGS["vanilla"]
+    dev = torch.device("cuda:0")
+    dw = E.random_device_weights(shape, seed=0, device=dev)
+    prompts = torch.from_numpy(synth.gen_prompts(shape, run)).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    points = []
+    for frac in cfg["active_fractions"]:
+        M = int(round(frac * N))
+        act = np.sort(np.random.default_rng(2).choice(N, size=M, replace=False))
+        locked = np.ones(N, dtype=bool)
+        locked[act] = False
+        words = np.zeros((1, (N + 63) // 64), dtype=np.uint64)
+        for p_ in np.nonzero(locked)[0]:
+            words[0, p_ // 64] |= np.uint64(1) << np.uint64(p_ % 64)
+        bits = torch.from_numpy(words.view(np.int64)).to(dev)
+        engs = []
+        for _ in range(n_caches):
+            e = E.Engine(shape, dw, run, lock, prompts)
+            kc, vc = e.kv_cache()
+            kc.copy_(torch.randn(kc.shape, generator=g, device=dev).to(kc.dtype))
+            vc.copy_(torch.randn(vc.shape, generator=g, device=dev).to(vc.dtype))
+            e.lock_bits().copy_(bits)
+            engs.append(e)
+
+        def go(n):
+            for i in range(n):
+                e = engs[i % n_caches]
+                assert e.step() == M
+                e.lock_update()
+
+        go(warmup)
+        for e in engs:
+            e.set_timing(True)
+        go(launches)
+        tot = {}
+        for e in engs:
+            for k, v in e.read_timing().items():
+                a = tot.setdefault(k, dict(ms=0.0, launches=0, bytes=0.0, flops=0.0))
+                for f in a:
+                    a[f] += v[f]
+            e.close()
+        gem = [tot[c] for c in GEMM_CLASSES]
+        g_s = sum(x["ms"] for x in gem) / 1e3 / launches
+        g_fl = sum(x["flops"] for x in gem) / launches
+        g_by = sum(x["bytes"] for x in gem) / launches
+        at = tot["attention"]
+        a_s = at["ms"] / 1e3 / max(at["launches"], 1)
+        a_by = at["bytes"] / max(at["launches"], 1)
+        a_fl = at["flops"] / max(at["launches"], 1)
+        pt = dict(M=M, gemm_us=round(g_s * 1e6, 2),
+                  gemm_tflops=round(g_fl / g_s / 1e12, 1),
+                  gemm_mfma_frac=round(g_fl / g_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  gemm_weight_stream_gbs=round(g_by / g_s / 1e9, 1),
+                  gemm_hbm_frac=round(g_by / g_s / 1e9 / PEAK_HBM_GBS, 4),
+                  attention_us=round(a_s * 1e6, 2),
+                  attention_gbs=round(a_by / a_s / 1e9, 1),
+                  attention_hbm_frac=round(a_by / a_s / 1e9 / PEAK_HBM_GBS, 4),
+                  attention_tflops=round(a_fl / a_s / 1e12, 1))
+        pt.update({f"{c}_us": round(tot[c]["ms"] * 1e3 / max(tot[c]["launches"], 1), 2)
+                   for c in GEMM_CLASSES + ("rmsnorm",)})
+        log(f"[layer M={M}] {pt}")
+        points.append(pt)
+        del engs
+        torch.cuda.empty_cache()
+    return dict(workload=("one bf16 LLaDA-8B-width layer (d=4096, 32x128 MHA, SwiGLU 12288) "
+                          f"over an N={N} cache, {n_caches} caches stepped round-robin, "
+                          f"{launches} timed launches per point"),
+                points=points)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +234,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-settings", action="store_true")
+    ap.add_argument("--no-layer-sweep", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the step engine has no multi-GPU path "
@@ -215,6 +309,9 @@ def main():
         out[f"{s}_lock"] = dict(steps_per_s=round(K / r["seconds"], 3),
                                 tokens_per_s=round(r["tokens"] / r["seconds"], 2),
                                 mean_active_rows=round(sum(r["ms"]) / len(r["ms"]), 1))
+    if not args.no_layer_sweep:
+        log("single-layer roofline sweep ...")
+        out["layer_isolation"] = layer_isolation()
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(shape, run)

@@ -31,6 +31,8 @@ namespace dlm {
 constexpr int kAttnQ = 64;     // query vectors per workgroup
 constexpr int kAttnKeys = 64;  // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyMax = 8.f;  // log2 headroom before the running maximum is raised
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int HD, bool SPLIT>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(
@@ -205,9 +207,31 @@ __device__ __forceinline__ void attn_dma16(const void* g, unsigned char* lds) {
 // Slot XORs measured conflict-free on gfx950 (SQ_LDS_BANK_CONFLICT): 16-byte
 // reads of 16 consecutive K rows at one chunk -> r & 15 (256-byte rows) or
 // r & 7 (128-byte rows); 8-byte reads of 16 consecutive V^T rows ->
-// (r & 7) ^ ((r >> 3) & 1).
+// (r & 7) ^ ((r >> 3) & 1).  (The compiler pairs V^T reads whose addresses
+// differ by a multiple of 512 bytes into ds_read2st64_b64, whose two halves
+// share banks; that pairing, not the XOR, leaves two-way conflicts there.)
 __device__ __forceinline__ int kswz(int r, int chunks) { return chunks == 16 ? (r & 15) : (r & 7); }
 __device__ __forceinline__ int vswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Reductions over the lanes l, l^16, l^32, l^48 with the gfx950 lane-swap
+// instructions: permlane16_swap(v, v) returns v from lanes l and l^16 in its
+// two outputs, permlane32_swap(v, v) from lanes l and l^32.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int N>
 __device__ __forceinline__ void attn_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
@@ -321,35 +345,44 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[kb], 0, 0, 0);
       }
     }
+    // Online softmax in base 2 on the scaled scores.  The running maximum of
+    // a query is raised (and its accumulators rescaled) only when the tile
+    // maximum exceeds it by more than kLazyMax; otherwise the exponentials
+    // are taken against the stale maximum and stay below 2^kLazyMax.  The
+    // normalised result is the same either way.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[kb][i] *= scale;
-        mx = fmaxf(mx, s[kb][i]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);  // m_run = -inf -> 0
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
+    mx *= scale;
+    if (__any(mx > m_run + kLazyMax)) {  // wave-uniform branch
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // m_run = -inf -> 0
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) oacc[cb] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
     s16x4 pb[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[kb][i] - m_new);
-        psum += p;
-        pb[kb][i] = (short)f2bf(p);
+        p[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], scale, -m_run));
+        psum += p[i];
       }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+      const u32x2 w = {f2bf2(p[0], p[1]), f2bf2(p[2], p[3])};
+      pb[kb] = __builtin_bit_cast(s16x4, w);
+    }
+    psum = xor32_sum(xor16_sum(psum));
+    l_run += psum;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      oacc[cb] *= alpha;
       const int vr = cb * 16 + (lane & 15);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
