@@ -30,7 +30,8 @@ EXPORTS = [
     "dlm_read_timing", "dlm_op_compact", "dlm_op_embed_rmsnorm", "dlm_op_rmsnorm",
     "dlm_op_gemm_ws_bytes", "dlm_op_gemm", "dlm_op_gemm_num_configs", "dlm_op_gemm_config",
     "dlm_op_rope_table", "dlm_op_rope_scatter",
-    "dlm_op_attention_ws_bytes", "dlm_op_attention", "dlm_op_vocab_ws_bytes",
+    "dlm_op_attention_ws_bytes", "dlm_op_attention", "dlm_op_attention_config_ws_bytes",
+    "dlm_op_attention_config", "dlm_op_vocab_ws_bytes",
     "dlm_op_vocab_stats", "dlm_op_commit_lock",
 ]
 
@@ -113,6 +114,9 @@ def lib() -> ctypes.CDLL:
         L.dlm_op_attention_ws_bytes.restype = sz
         L.dlm_op_attention_ws_bytes.argtypes = [i32] * 7
         L.dlm_op_attention.argtypes = [i32] * 7 + [vp] * 5 + [vp, sz, vp]
+        L.dlm_op_attention_config_ws_bytes.restype = sz
+        L.dlm_op_attention_config_ws_bytes.argtypes = [i32] * 8
+        L.dlm_op_attention_config.argtypes = [i32] * 7 + [vp] * 5 + [i32, i32, vp, sz, vp]
         L.dlm_op_vocab_ws_bytes.restype = sz
         L.dlm_op_vocab_ws_bytes.argtypes = [i32, i32]
         L.dlm_op_vocab_stats.argtypes = [i32, i32, i32, i32, i32] + [vp] * 14 + [sz, vp]

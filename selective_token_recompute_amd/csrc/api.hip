@@ -708,6 +708,30 @@ int dlm_op_attention(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, i
                                      vcache, o, ws, ws ? ws_bytes : 0, (hipStream_t)stream));
 }
 
+size_t dlm_op_attention_config_ws_bytes(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len,
+                                        int32_t nq, int32_t nkv, int32_t hd, int32_t splits) {
+  if (!dt_ok(dtype) || M < 0 || batch < 1 || seq_len < 1 || nq < 1 || nkv < 1 || nq % nkv ||
+      splits < 0)
+    return 0;
+  return attention_cfg_ws_bytes(dtype, M, batch, seq_len, nq, nkv, hd, splits);
+}
+
+int dlm_op_attention_config(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, int32_t nq,
+                            int32_t nkv, int32_t hd, const void* q, const int32_t* row_start,
+                            const void* kcache, const void* vcache, void* o, int32_t splits,
+                            int32_t stages, void* ws, size_t ws_bytes, void* stream) {
+  if (!dt_ok(dtype) || M < 0 || batch < 1 || seq_len < 1 || nq < 1 || nkv < 1 || nq % nkv ||
+      hd < 2 || hd > 256 || (hd & 1) || splits < 0 || (stages != 0 && stages != 2 && stages != 4))
+    return DLM_E_INVALID;
+  if (M == 0) return DLM_OK;
+  if (!q || !row_start || !kcache || !vcache || !o) return DLM_E_INVALID;
+  if (attention_cfg_ws_bytes(dtype, M, batch, seq_len, nq, nkv, hd, splits) > (ws ? ws_bytes : 0))
+    return DLM_E_SIZE;
+  return hip_status(launch_attention_cfg(dtype, M, batch, seq_len, nq, nkv, hd, q, row_start,
+                                         kcache, vcache, o, ws, ws ? ws_bytes : 0, splits, stages,
+                                         (hipStream_t)stream));
+}
+
 size_t dlm_op_vocab_ws_bytes(int32_t M, int32_t V) {
   if (M < 0 || V < 1) return 0;
   return vocab_ws_bytes(M, V);

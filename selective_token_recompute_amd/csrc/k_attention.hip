@@ -234,7 +234,26 @@ __device__ __forceinline__ float xor32_sum(float v) {
 
 template <int N>
 __device__ __forceinline__ void attn_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Waits until at most n (0 <= n < S) tiles of IPW load instructions each are
+// still in flight for this wave.
+template <int IPW, int S>
+__device__ __forceinline__ void attn_wait_tiles(int n) {
+  if constexpr (S <= 1) {
+    attn_wait_vmcnt<0>();
+  } else {
+    if (n >= S - 1) attn_wait_vmcnt<(S - 1) * IPW>();
+    else attn_wait_tiles<IPW, S - 1>(n);
+  }
+}
+// Workgroup barrier without the vmcnt(0) of __syncthreads(); the empty asm
+// statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void attn_lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int HD, bool SPLIT, int STAGES>
@@ -263,21 +282,9 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
 
   const int qv = qbase + wave * 16 + (lane & 15);
   const bool qok = qv < Qn;
+  const bool wave_live = qbase + wave * 16 < Qn;  // wave-uniform
   const int row = r0 + (qok ? qv / G : 0);
   const int head = g * G + (qok ? qv % G : 0);
-  bf16x8 qf[NKC];
-  {
-    const bf16_t* qp = q + (size_t)row * nq * HD + (size_t)head * HD + (lane >> 4) * 8;
-#pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      if (qok) {
-        qf[c] = *(const bf16x8*)(qp + c * 32);
-      } else {
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        qf[c] = *(const bf16x8*)&z;
-      }
-    }
-  }
   const size_t slab = ((size_t)b * nkv + g) * N * HD;
   const bf16_t* kslab = kc + slab;  // [N][HD]
   const bf16_t* vslab = vc + slab;  // [HD][N]
@@ -323,14 +330,28 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
     if (t < ntiles) issue(t);
+  // the query fragments load while the first tiles are in flight
+  bf16x8 qf[NKC];
+  {
+    const bf16_t* qp = q + (size_t)row * nq * HD + (size_t)head * HD + (lane >> 4) * 8;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      if (qok) {
+        qf[c] = *(const bf16x8*)(qp + c * 32);
+      } else {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        qf[c] = *(const bf16x8*)&z;
+      }
+    }
+  }
+
   for (int t = 0; t < ntiles; ++t) {
-    // this wave's loads of tile t (later tiles may stay in flight)
-    const int ahead = min(STAGES - 2, ntiles - 1 - t);
-    if (STAGES >= 4 && ahead >= 2) attn_wait_vmcnt<2 * IPW>();
-    else if (STAGES >= 3 && ahead >= 1) attn_wait_vmcnt<IPW>();
-    else attn_wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();   // everyone's loads of t; everyone done with t-1
+    // this wave's loads of tile t (later tiles may stay in flight), then
+    // everyone's; every wave is done with tile t-1 after the barrier
+    attn_wait_tiles<IPW, STAGES - 1>(min(STAGES - 2, ntiles - 1 - t));
+    attn_lds_barrier();
     if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1);
+    if (!wave_live) continue;  // no query of this wave is valid: loads only
     const unsigned char* st = smem + (t % STAGES) * STAGE;
     f32x4 s[4];
 #pragma unroll
@@ -400,9 +421,7 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
     const size_t base = (size_t)blockIdx.z * M * nq + gq;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        part_o[base * HD + cb * 16 + (lane >> 4) * 4 + i] = oacc[cb][i];
+      *(f32x4*)(part_o + base * HD + cb * 16 + (lane >> 4) * 4) = oacc[cb];
     if ((lane >> 4) == 0) {
       part_ml[base * 2] = m_run;
       part_ml[base * 2 + 1] = l_run;
@@ -423,28 +442,33 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
   }
 }
 
-// Combine split-KV partials: o = sum_s o_s 2^(m_s - m) / sum_s l_s 2^(m_s - m).
+// Combine split-KV partials: o = sum_s o_s 2^(m_s - m) / sum_s l_s 2^(m_s - m),
+// m = max_s m_s; one thread per 4 consecutive output columns.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            int splits, int MQ, int hd,
                                                            T* __restrict__ o) {
-  const size_t total = (size_t)MQ * hd;
+  const int hd4 = hd / 4;
+  const size_t total = (size_t)MQ * hd4;
   for (size_t f = blockIdx.x * (size_t)blockDim.x + threadIdx.x; f < total;
        f += (size_t)gridDim.x * blockDim.x) {
-    const size_t gq = f / hd;
-    const int c = (int)(f % hd);
+    const size_t gq = f / hd4;
+    const int c = (int)(f % hd4) * 4;
     float m = -INFINITY;
     for (int s = 0; s < splits; ++s) m = fmaxf(m, part_ml[((size_t)s * MQ + gq) * 2]);
-    float den = 0.f, num = 0.f;
+    float den = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < splits; ++s) {
       const float ms = part_ml[((size_t)s * MQ + gq) * 2];
       if (ms == -INFINITY) continue;
       const float w = exp2f(ms - m);
       den += part_ml[((size_t)s * MQ + gq) * 2 + 1] * w;
-      num += part_o[((size_t)s * MQ + gq) * hd + c] * w;
+      num += *(const f32x4*)(part_o + ((size_t)s * MQ + gq) * hd + c) * w;
     }
-    st(o, f, num / den);
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st(o, gq * hd + c + i, num[i] * inv);
   }
 }
 
@@ -501,15 +525,25 @@ namespace {
 
 struct AttnPlan {
   bool mfma;
-  int qtiles, splits, keys_per_split;
+  int qtiles, splits, keys_per_split, stages;
   size_t ws;
 };
 
-AttnPlan make_attn_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd) {
+constexpr size_t kAttnSplitCap = 64ull << 20;  // split-KV partials never exceed this
+
+// Splits the keys while fewer than 128 workgroups would be busy (the
+// combine pass costs a launch plus a write and a read of every partial
+// output), keeping at least one 64-key tile per split, and uses a 2-stage
+// LDS ring (64 KB at hd 128).  Both choices come from a sweep on MI355X over
+// M = 20 .. 1024 active rows and N = 512, 1024 keys (32 heads of 128), where
+// 2 stages beat 4 at every point and more splits lost to the combine pass.
+AttnPlan make_attn_plan_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits_in,
+                            int stages_in) {
   AttnPlan p{};
   p.mfma = dtype == kBF16 && (hd == 64 || hd == 128) && nq % nkv == 0;
   p.splits = 1;
   p.keys_per_split = N;
+  p.stages = 4;
   if (!p.mfma || M <= 0) return p;
   const int G = nq / nkv;
   const int mb_max = std::min(M, N);  // rows of one sequence
@@ -517,37 +551,52 @@ AttnPlan make_attn_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd)
   // estimated busy workgroups: the rows are spread over the sequences
   const int busy = std::max(1, (M * G + kAttnQ - 1) / kAttnQ) * nkv;
   const int ktiles = (N + kAttnKeys - 1) / kAttnKeys;
-  // split the keys only when few workgroups would run (the combine pass
-  // costs a write and a read of every partial output)
+  auto ws_of = [&](int sp) { return (size_t)sp * M * nq * (hd + 2) * sizeof(float); };
   int splits = 1;
-  while (busy * splits < 128 && ktiles / (splits * 2) >= 2 &&
-         (size_t)(splits * 2) * M * nq * (hd + 2) * sizeof(float) <= (64ull << 20))
-    splits *= 2;
+  if (splits_in > 0) {
+    splits = std::min(splits_in, ktiles);
+  } else {
+    while (busy * splits < 128 && ktiles / (splits * 2) >= 1 && ws_of(splits * 2) <= kAttnSplitCap)
+      splits *= 2;
+  }
   p.splits = splits;
-  p.keys_per_split = ((ktiles + splits - 1) / splits) * kAttnKeys;
-  p.ws = splits > 1 ? (size_t)splits * M * nq * (hd + 2) * sizeof(float) : 0;
+  const int tiles_per = (ktiles + splits - 1) / splits;
+  p.keys_per_split = tiles_per * kAttnKeys;
+  p.stages = stages_in == 2 || stages_in == 4 ? stages_in : 2;
+  p.ws = splits > 1 ? ws_of(splits) : 0;
   return p;
 }
 
+AttnPlan make_attn_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd) {
+  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, 0, 0);
+}
+
+template <int HD, bool SPLIT, int STAGES>
+void launch_attn_dma(dim3 grid, const void* q, const int32_t* row_start, const void* kc,
+                     const void* vc, void* o, int N, int nq, int nkv, int kps, int M, float* po,
+                     float* pml, hipStream_t s) {
+  constexpr size_t lds = STAGES * (size_t)(2 * kAttnKeys * HD * 2);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attn_mfma_dma_kernel<HD, SPLIT, STAGES>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    attr = true;
+  }
+  attn_mfma_dma_kernel<HD, SPLIT, STAGES><<<grid, 256, lds, s>>>(
+      (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq, nkv,
+      kps, M, po, pml);
+}
+
 template <int HD, bool SPLIT>
-void launch_attn_kernel(dim3 grid, bool dma, const void* q, const int32_t* row_start,
+void launch_attn_kernel(dim3 grid, bool dma, int stages, const void* q, const int32_t* row_start,
                         const void* kc, const void* vc, void* o, int N, int nq, int nkv,
                         int kps, int M, float* po, float* pml, hipStream_t s) {
   if (dma) {
-    // 4 stages (128 KB of LDS at hd 128, one workgroup per CU) keep three
-    // tiles in flight
-    constexpr int STAGES = HD == 128 ? 4 : 4;
-    constexpr size_t lds = STAGES * (size_t)(2 * kAttnKeys * HD * 2);
-    static bool attr = false;
-    if (!attr) {
-      (void)hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&attn_mfma_dma_kernel<HD, SPLIT, STAGES>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      attr = true;
-    }
-    attn_mfma_dma_kernel<HD, SPLIT, STAGES><<<grid, 256, lds, s>>>(
-        (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq,
-        nkv, kps, M, po, pml);
+    if (stages == 2)
+      launch_attn_dma<HD, SPLIT, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
+    else
+      launch_attn_dma<HD, SPLIT, 4>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
   } else {
     attn_mfma_kernel<HD, SPLIT><<<grid, 256, 0, s>>>((const bf16_t*)q, row_start,
                                                      (const bf16_t*)kc, (const bf16_t*)vc,
@@ -564,15 +613,15 @@ hipError_t run_attn_mfma(const AttnPlan& p, int M, int B, int N, int nq, int nkv
   if (p.splits > 1) {
     float* po = (float*)ws;
     float* pml = po + (size_t)p.splits * M * nq * HD;
-    launch_attn_kernel<HD, true>(grid, dma, q, row_start, kc, vc, o, N, nq, nkv,
+    launch_attn_kernel<HD, true>(grid, dma, p.stages, q, row_start, kc, vc, o, N, nq, nkv,
                                  p.keys_per_split, M, po, pml, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t total = (size_t)M * nq * HD;
+    const size_t total = (size_t)M * nq * (HD / 4);
     const int gsz = (int)std::min<size_t>((total + 255) / 256, 8192);
     attn_combine_kernel<bf16_t><<<gsz, 256, 0, s>>>(po, pml, p.splits, M * nq, HD, (bf16_t*)o);
   } else {
-    launch_attn_kernel<HD, false>(grid, dma, q, row_start, kc, vc, o, N, nq, nkv,
+    launch_attn_kernel<HD, false>(grid, dma, p.stages, q, row_start, kc, vc, o, N, nq, nkv,
                                   p.keys_per_split, M, nullptr, nullptr, s);
   }
   return hipGetLastError();
@@ -584,11 +633,12 @@ size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int h
   return make_attn_plan(dtype, M, B, N, nq, nkv, hd).ws;
 }
 
-hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int hd,
-                            const void* q, const int32_t* row_start, const void* kc,
-                            const void* vc, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
+hipError_t launch_attention_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd,
+                                const void* q, const int32_t* row_start, const void* kc,
+                                const void* vc, void* o, void* ws, size_t ws_bytes, int splits,
+                                int stages, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  AttnPlan p = make_attn_plan(dtype, M, B, N, nq, nkv, hd);
+  AttnPlan p = make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, stages);
   if (p.mfma && p.ws > ws_bytes) {
     p.splits = 1;
     p.keys_per_split = N;
@@ -608,6 +658,17 @@ hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int
                                                     (const float*)kc, (const float*)vc,
                                                     (float*)o, M, N, nq, nkv, hd);
   return hipGetLastError();
+}
+
+hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int hd,
+                            const void* q, const int32_t* row_start, const void* kc,
+                            const void* vc, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
+  return launch_attention_cfg(dtype, M, B, N, nq, nkv, hd, q, row_start, kc, vc, o, ws, ws_bytes,
+                              0, 0, s);
+}
+
+size_t attention_cfg_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits) {
+  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, 0).ws;
 }
 
 }  // namespace dlm
