@@ -79,26 +79,78 @@ def run_steps(eng_factory, K, timing=False):
 
 
 def roofline_entry(tim, setting_ms):
-    # dominant class by total event time
+    """Roofline of the kernel class with the largest event time: the class's
+    algorithmic FLOPs / bytes per launch over its average launch duration,
+    both from the engine's HIP events around each launch (the events include
+    the few microseconds between back-to-back dispatches on one queue, which
+    a kernel trace's durations do not)."""
     name = max(tim, key=lambda k: tim[k]["ms"])
     t = tim[name]
     avg_s = t["ms"] / 1e3 / max(t["launches"], 1)
     flops = t["flops"] / max(t["launches"], 1)
     byts = t["bytes"] / max(t["launches"], 1)
     mean_m = sum(setting_ms) / len(setting_ms)
+    timing = "engine HIP events around each launch over the timed steps"
     if flops > 0 and flops / max(byts, 1.0) >= RIDGE:
         ach = flops / avg_s / 1e12
         return name, dict(bound="mfma", achieved=round(ach, 2), peak=PEAK_BF16_TFLOPS,
                           unit="TFLOP/s", frac=round(ach / PEAK_BF16_TFLOPS, 4), traffic=None,
                           kernel=name, avg_launch_us=round(avg_s * 1e6, 2),
                           flops_per_launch=flops, bytes_per_launch=byts,
-                          launches=t["launches"], mean_active_rows=round(mean_m, 1))
+                          launches=t["launches"], mean_active_rows=round(mean_m, 1),
+                          timing=timing)
     ach = byts / avg_s / 1e9
     return name, dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                       frac=round(ach / PEAK_HBM_GBS, 4), traffic=None, kernel=name,
                       avg_launch_us=round(avg_s * 1e6, 2), flops_per_launch=flops,
                       bytes_per_launch=byts, launches=t["launches"],
-                      mean_active_rows=round(mean_m, 1))
+                      mean_active_rows=round(mean_m, 1), timing=timing)
+
+
+TRAFFIC_SOURCES = ("selective_token_recompute_amd/csrc/k_gemm.hip",
+                   "selective_token_recompute_amd/csrc/common.h")
+
+
+def sources_sha256(paths=TRAFFIC_SOURCES):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel_class):
+    """HBM bytes per launch of a kernel class from the committed counter
+    summary profiles/<class>_traffic.md (lines 'key: value'), or None when
+    the summary is missing or the kernel sources changed since the counters
+    were taken (sha256 over TRAFFIC_SOURCES)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_class}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("sources_sha256") != sources_sha256():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of nbytes (torch's copy kernel), reps
+    times: the reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
 
 
 def cpu_baseline(shape, run):
@@ -235,6 +287,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-settings", action="store_true")
     ap.add_argument("--no-layer-sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 1 GiB device copies (counter calibration for profiles)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the step engine has no multi-GPU path "
@@ -270,6 +324,7 @@ def main():
     # per-kernel event timing over the same steps (configured setting)
     _, _, ms_nat, tim = run_steps(factory("natural"), K, timing=True)
     dom, roof = roofline_entry(tim, ms_nat)
+    roof["traffic"] = measured_traffic(dom)
     kernels = {k: dict(ms_total=round(v["ms"], 3), launches=v["launches"],
                        us_avg=round(v["ms"] * 1e3 / max(v["launches"], 1), 2))
                for k, v in tim.items() if v["launches"]}
@@ -315,6 +370,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(shape, run)
+    if args.copy_calibration:
+        copy_calibration()
     print(json.dumps(out), flush=True)
 
 

@@ -387,8 +387,9 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out) {
   const float* part = (const float*)ws;
   int sp_res = 0;  // split-K partials of the last residual update, pending
   for (int l = 0; l < m.n_layers; ++l) {
+    // residual norm: read h and the pending split-K partials, write h and y
     if (l > 0)
-      TRY(timed(h, DLM_K_RMSNORM, M * (double)d * (4 + es), 0.0, [&] {
+      TRY(timed(h, DLM_K_RMSNORM, M * (double)d * (4.0 * (2 + sp_res) + es), 0.0, [&] {
         return launch_rmsnorm_resid(dt, M, d, m.rms_eps, hres, part, sp_res, h->attn_norm[l], a,
                                     s);
       }));
@@ -421,13 +422,13 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out) {
       }));
     }
     TRY(gemm(DLM_K_GEMM_O, kEpiResidAdd, d, qo, o, h->w_o[l], nullptr, hres, &sp_res));
-    TRY(timed(h, DLM_K_RMSNORM, M * (double)d * (4 + es), 0.0, [&] {
+    TRY(timed(h, DLM_K_RMSNORM, M * (double)d * (4.0 * (2 + sp_res) + es), 0.0, [&] {
       return launch_rmsnorm_resid(dt, M, d, m.rms_eps, hres, part, sp_res, h->ffn_norm[l], a, s);
     }));
     TRY(gemm(DLM_K_GEMM_GATE_UP, kEpiSwiglu, dff, d, a, h->w_gate[l], h->w_up[l], u, nullptr));
     TRY(gemm(DLM_K_GEMM_DOWN, kEpiResidAdd, d, dff, u, h->w_down[l], nullptr, hres, &sp_res));
   }
-  TRY(timed(h, DLM_K_RMSNORM, M * (double)d * (4 + es), 0.0, [&] {
+  TRY(timed(h, DLM_K_RMSNORM, M * (double)d * (4.0 * (2 + sp_res) + es), 0.0, [&] {
     return launch_rmsnorm_resid(dt, M, d, m.rms_eps, hres, part, sp_res, h->fnorm, a, s);
   }));
   float* zc = h->at<float>(y.z[cur]);

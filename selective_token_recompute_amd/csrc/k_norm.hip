@@ -8,6 +8,8 @@
 // subset's cache entries.  The model details (pre-RMSNorm, half-split rotary
 // embedding) are not on the pages; they follow the LLaDA-style architecture
 // the experiments use.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -49,13 +51,15 @@ __device__ __forceinline__ float4 ld4<bf16_t>(const bf16_t* p, size_t i) {
   return make_float4(bf2f(w.x), bf2f(w.y), bf2f(w.z), bf2f(w.w));
 }
 
-template <typename T, bool kGather>
+template <typename T, bool kGather, int SP>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_vec_kernel(
     int M, int d, int N, float eps, int mask_id, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
     const T* __restrict__ emb, const T* __restrict__ g, float* __restrict__ h,
     const float* __restrict__ partial, int splits, T* __restrict__ y,
     int32_t* __restrict__ row_real) {
+  // SP: compile-time bound on the split-K partials (splits <= SP), so that
+  // every load of a row is independent and in flight at once
   constexpr int MAXV = 4;
   __shared__ float red[16];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_vec_kernel(
     src = emb + (size_t)tok * d;
   }
   float4 v[MAXV];
-  float ss = 0.f;
+  float4 pp[SP > 0 ? SP : 1][MAXV];
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int c4 = tid + i * kNormThreads;
@@ -78,12 +82,27 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_vec_kernel(
         v[i] = ld4(src, (size_t)c4 * 4);
       } else {
         v[i] = *(const float4*)(hr + (size_t)c4 * 4);
-        for (int sp = 0; sp < splits; ++sp) {
-          const float4 p = *(const float4*)(partial + ((size_t)sp * M + r) * d + (size_t)c4 * 4);
-          v[i].x += p.x;
-          v[i].y += p.y;
-          v[i].z += p.z;
-          v[i].w += p.w;
+#pragma unroll
+        for (int sp = 0; sp < SP; ++sp)
+          pp[sp][i] = sp < splits ? *(const float4*)(partial + ((size_t)sp * M + r) * d +
+                                                     (size_t)c4 * 4)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c4 = tid + i * kNormThreads;
+    if (c4 < d4) {
+      if (!kGather) {
+        // partials summed in split order, as the split-K reduction does
+#pragma unroll
+        for (int sp = 0; sp < SP; ++sp) {
+          v[i].x += pp[sp][i].x;
+          v[i].y += pp[sp][i].y;
+          v[i].z += pp[sp][i].z;
+          v[i].w += pp[sp][i].w;
         }
       }
       if (kGather || splits > 0) *(float4*)(hr + (size_t)c4 * 4) = v[i];
@@ -145,11 +164,19 @@ hipError_t run_norm(int M, int d, int N, float eps, int mask_id, const int32_t* 
                     const void* g, float* h, const float* partial, int splits, void* y,
                     int32_t* row_real, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (d % 4 == 0 && d <= 16 * kNormThreads)
-    rmsnorm_vec_kernel<T, kGather><<<M, kNormThreads, 0, s>>>(
-        M, d, N, eps, mask_id, tokens, row_seq, row_pos, (const T*)emb, (const T*)g, h, partial,
-        splits, (T*)y, row_real);
-  else
+  if (d % 4 == 0 && d <= 16 * kNormThreads && splits <= 8) {
+    auto go = [&](auto sp_tag) {
+      constexpr int SP = decltype(sp_tag)::value;
+      rmsnorm_vec_kernel<T, kGather, SP><<<M, kNormThreads, 0, s>>>(
+          M, d, N, eps, mask_id, tokens, row_seq, row_pos, (const T*)emb, (const T*)g, h,
+          partial, splits, (T*)y, row_real);
+    };
+    if (kGather || splits == 0) go(std::integral_constant<int, 0>{});
+    else if (splits == 1) go(std::integral_constant<int, 1>{});
+    else if (splits == 2) go(std::integral_constant<int, 2>{});
+    else if (splits <= 4) go(std::integral_constant<int, 4>{});
+    else go(std::integral_constant<int, 8>{});
+  } else
     rmsnorm_kernel<T, kGather><<<M, kNormThreads, 0, s>>>(
         M, d, N, eps, mask_id, tokens, row_seq, row_pos, (const T*)emb, (const T*)g, h, partial,
         splits, (T*)y, row_real);
