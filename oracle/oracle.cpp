@@ -523,7 +523,9 @@ int orc_lock_update(orc_state* s, const int32_t* ov_commit_seq, const int32_t* o
                     const int32_t* ov_commit_tok, int32_t n_ov_commit,
                     const uint8_t* ov_locked /* [B][N] or null */,
                     const int32_t* ov_cnt /* [B][N] or null */) {
-  if (!s->stepped || s->partial) return -4;
+  // after a sampled step only a fully overridden transition is defined (the
+  // rule would read statistics that exist for the sampled rows only)
+  if (!s->stepped || (s->partial && !(n_ov_commit >= 0 && ov_locked != nullptr))) return -4;
   const orc_run& r = s->r;
   s->commit_seq.clear();
   s->commit_pos.clear();

@@ -47,6 +47,10 @@ def test_tiny_fp32_kl_reverse_direction(tiny):
 MID = synth.ModelShape(2, 512, 4, 4, 128, 1024, 4096, bf16=True)
 MID_GQA = synth.ModelShape(2, 512, 8, 2, 128, 1024, 4000, bf16=True)
 MID_RUN = synth.RunShape(2, 192, 64, 32, 64)   # two sequences, 2 semi-AR blocks
+# Dream-7B's head grouping (7 query heads per K/V head) at small width, three
+# sequences of different prompt content, two semi-AR blocks
+MID_G7 = synth.ModelShape(2, 896, 7, 1, 128, 2368, 4000, bf16=True)
+MID_G7_RUN = synth.RunShape(3, 160, 32, 32, 64)
 
 
 @pytest.mark.parametrize("shape", [MID, MID_GQA], ids=["mha", "gqa"])
@@ -56,6 +60,14 @@ def test_mid_bf16_mfma_path(shape, setting):
     pr = synth.gen_prompts(shape, MID_RUN)
     reps = run_lockstep(shape, W, MID_RUN, synth.LOCK_SETTINGS[setting], pr)
     _report(f"mid-{shape.n_kv_heads}/{setting}", reps)
+
+
+@pytest.mark.parametrize("setting", ["scheduled", "natural"])
+def test_mid_bf16_group7_batched(setting):
+    W = synth.gen_weights(MID_G7)
+    pr = synth.gen_prompts(MID_G7, MID_G7_RUN)
+    reps = run_lockstep(MID_G7, W, MID_G7_RUN, synth.LOCK_SETTINGS[setting], pr)
+    _report(f"mid-g7/{setting}", reps)
 
 
 def test_tiny_bf16_generic_path():
