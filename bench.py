@@ -279,6 +279,42 @@ def layer_isolation(n_caches=32, launches=100, warmup=10):
                 points=points)
 
 
+EXTRA_CONFIGS = {
+    "dream7b": "Dream-7B shape (28 layers, d=3584, 28 query / 4 K-V heads x128, SwiGLU 18944, "
+               "vocab 152064, bf16), B=8 sequences of N=1024 (256 prompt + 768 masked), 256-step "
+               "runs, one semi-AR block",
+    "longctx": "LLaDA-8B shape, B=4 sequences of N=4096 (1024 prompt + 3072 masked), 512-step runs "
+               "in 12 semi-AR blocks of 256",
+}
+
+
+def extra_config(name, K, full_run=False, settings=("natural", "scheduled")):
+    """Steps/s and tokens/s of another configured shape: the first K steps of
+    a run (M at its largest), or whole runs with full_run."""
+    import torch
+    import synth
+    from selective_token_recompute_amd import engine as E
+    shape, run = synth.CONFIGS[name]
+    dev = torch.device("cuda:0")
+    dw = E.random_device_weights(shape, seed=0, device=dev)
+    prompts = torch.from_numpy(synth.gen_prompts(shape, run)).to(dev)
+    out = dict(workload=EXTRA_CONFIGS[name], batch=run.batch, seq_len=run.seq_len)
+    steps = run.steps if full_run else K
+    for st in settings:
+        def factory():
+            return E.Engine(shape, dw, run, synth.LOCK_SETTINGS[st], prompts)
+        run_steps(factory, 2)
+        dt, toks, ms, _ = run_steps(factory, steps)
+        out[st] = dict(steps=steps, from_run_start=True, steps_per_s=round(steps / dt, 3),
+                       tokens_per_s=round(toks / dt, 2), ms_per_step=round(dt * 1e3 / steps, 2),
+                       mean_active_rows=round(sum(ms) / len(ms), 1), first_m=ms[0])
+        log(f"[{name}/{st}] {steps} steps in {dt:.2f} s -> {steps / dt:.2f} steps/s, "
+            f"{toks / dt:.1f} tokens/s, mean M {sum(ms) / len(ms):.1f}")
+    del dw
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +323,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-settings", action="store_true")
     ap.add_argument("--no-layer-sweep", action="store_true")
+    ap.add_argument("--extra-configs", default="dream7b,longctx",
+                    help="other configured shapes to time ('' for none)")
+    ap.add_argument("--extra-steps", type=int, default=16)
+    ap.add_argument("--full-runs", action="store_true",
+                    help="time whole runs of the extra configurations")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 1 GiB device copies (counter calibration for profiles)")
     args = ap.parse_args()
@@ -364,6 +405,9 @@ def main():
         out[f"{s}_lock"] = dict(steps_per_s=round(K / r["seconds"], 3),
                                 tokens_per_s=round(r["tokens"] / r["seconds"], 2),
                                 mean_active_rows=round(sum(r["ms"]) / len(r["ms"]), 1))
+    for name in [c for c in args.extra_configs.split(",") if c]:
+        log(f"{name} ...")
+        out[name] = extra_config(name, args.extra_steps, args.full_runs)
     if not args.no_layer_sweep:
         log("single-layer roofline sweep ...")
         out["layer_isolation"] = layer_isolation()
