@@ -533,8 +533,22 @@ constexpr TileCfg kCfgs[] = {
     {64, 128, 4, 1, 8, 32},   // 21: one head per wave, 7 slices in flight
     {384, 128, 4, 2, 5, 32},  // 22: 8 waves
     {192, 128, 2, 2, 4, 64},  // 23
+    {192, 256, 2, 4, 2, 64},  // 24: 8 waves, 96x64 per wave
+    {384, 128, 4, 2, 2, 64},  // 25: 8 waves, 96x64 per wave
+    {128, 256, 2, 4, 2, 64},  // 26: 8 waves, 64x64 per wave
+    {192, 192, 2, 4, 2, 64},  // 27: 8 waves, 96x48 per wave (not for SwiGLU)
+    {192, 128, 2, 4, 3, 64},  // 28: 8 waves, 2 slices in flight
+    {192, 128, 2, 4, 4, 64},  // 29: 8 waves, 3 slices in flight
+    {192, 128, 4, 1, 3, 64},  // 30: one head per wave, 2 slices in flight
+    {192, 128, 4, 1, 4, 64},  // 31: one head per wave, 3 slices in flight
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+constexpr bool cfgs_fit_lds() {
+  for (const TileCfg& c : kCfgs)
+    if ((size_t)c.stages * (c.bm + c.bn) * c.bk * 2 > 160 * 1024) return false;
+  return true;
+}
+static_assert(cfgs_fit_lds(), "every tile configuration must fit the 160 KB of LDS of a CU");
 constexpr int kBK = 64;  // K granularity every configuration accepts
 constexpr size_t kSplitCapBytes = 64ull << 20;  // split-K partials never exceed this
 constexpr int kCUs = 256;
@@ -548,18 +562,20 @@ struct Plan {
   bool defer_reduce;  // split-K partials are left for the consumer kernel
 };
 
-// Default configuration by GEMM class and M bucket, from a sweep of every
-// configuration on MI355X at the LLaDA-8B shapes (QKV 4096->12288, O
+// Default configuration by GEMM class and M bucket, from sweeps of the
+// configurations on MI355X at the LLaDA-8B shapes (QKV 4096->12288, O
 // 4096->4096, gate/up 4096->2x12288, down 12288->4096, LM head
-// 4096->126464): small M favours narrow row tiles that stream the weights
-// with many workgroups; large M favours 2-stage tiles with two workgroups per
-// CU or 256x256 tiles with 8 waves.
+// 4096->126464) with the weights streamed from HBM: small M favours narrow
+// row tiles that stream the weights with many workgroups; around M = 384 the
+// gate/up and QKV projections favour 2-stage 4-wave tiles with two
+// workgroups per CU, the O / down projections and the LM head 8-wave tiles;
+// large M favours 256x256 tiles with 8 waves.
 int pick_cfg(int M, int N, bool dual) {
   static const int kBucket[] = {16, 32, 64, 128, 192, 256, 320, 384, 512};
-  static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 5, 5, 8, 13};
+  static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 28, 28, 8, 13};
   static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 9, 13};
   static const int kDual[] = {1, 1, 1, 8, 5, 9, 12, 12, 13, 13};
-  static const int kWide[] = {7, 7, 14, 10, 12, 13, 12, 12, 13, 13};
+  static const int kWide[] = {7, 7, 14, 10, 12, 13, 25, 25, 13, 13};
   int b = 0;
   while (b < 9 && M > kBucket[b]) ++b;
   if (dual) return kDual[b];
@@ -674,7 +690,15 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
     case 20: return run_mfma<64, 64, 2, 2, 8, 32, EPI>(a, p, ep, ws, s);
     case 21: return run_mfma<64, 128, 4, 1, 8, 32, EPI>(a, p, ep, ws, s);
     case 22: return run_mfma<384, 128, 4, 2, 5, 32, EPI>(a, p, ep, ws, s);
-    default: return run_mfma<192, 128, 2, 2, 4, 64, EPI>(a, p, ep, ws, s);
+    case 23: return run_mfma<192, 128, 2, 2, 4, 64, EPI>(a, p, ep, ws, s);
+    case 24: return run_mfma<192, 256, 2, 4, 2, 64, EPI>(a, p, ep, ws, s);
+    case 25: return run_mfma<384, 128, 4, 2, 2, 64, EPI>(a, p, ep, ws, s);
+    case 26: return run_mfma<128, 256, 2, 4, 2, 64, EPI>(a, p, ep, ws, s);
+    case 27: return run_mfma<192, 192, 2, 4, 2, 64, EPI>(a, p, ep, ws, s);
+    case 28: return run_mfma<192, 128, 2, 4, 3, 64, EPI>(a, p, ep, ws, s);
+    case 29: return run_mfma<192, 128, 2, 4, 4, 64, EPI>(a, p, ep, ws, s);
+    case 30: return run_mfma<192, 128, 4, 1, 3, 64, EPI>(a, p, ep, ws, s);
+    default: return run_mfma<192, 128, 4, 1, 4, 64, EPI>(a, p, ep, ws, s);
   }
 }
 

@@ -416,8 +416,8 @@ def test_gemm_every_tile_config(epi, splits):
     rs = torch.zeros(M, dtype=torch.int32, device=DEV)
     rp = torch.arange(M, dtype=torch.int32, device=DEV)
     for cfg in range(ops.num_gemm_configs()):
-        if epi == L.DLM_EPI_SWIGLU and cfg == 7:
-            continue  # 16-column wave tiles cannot pair gate and up columns
+        if epi == L.DLM_EPI_SWIGLU and cfg in (7, 27):
+            continue  # an odd number of 16-column wave tiles cannot pair gate and up
         for call in range(2):
             if epi == L.DLM_EPI_RESID_ADD:
                 h0 = synth.gen_normal((M, N), 5 + call, 1.0)
