@@ -78,12 +78,13 @@ size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int h
 hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int hd,
                             const void* q, const int32_t* row_start, const void* kc,
                             const void* vc, void* o, void* ws, size_t ws_bytes, hipStream_t s);
-// Same with a forced split-KV count and LDS stage count (0: the plan's).
+// Same with a forced split-KV count, LDS stage count and number of waves per
+// 16-query block (0: the plan's).
 size_t attention_cfg_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits);
 hipError_t launch_attention_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd,
                                 const void* q, const int32_t* row_start, const void* kc,
                                 const void* vc, void* o, void* ws, size_t ws_bytes, int splits,
-                                int stages, hipStream_t s);
+                                int stages, int key_halves, hipStream_t s);
 
 // ---- vocabulary statistics ----------------------------------------------------------
 size_t vocab_ws_bytes(int M, int V);

@@ -256,33 +256,40 @@ __device__ __forceinline__ void attn_lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int HD, bool SPLIT, int STAGES>
-__global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
+template <int HD, bool SPLIT, int STAGES, int KH>
+__global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ row_start,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ o, int N,
     int nq, int nkv, int keys_per_split, int M, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
+  // KH waves share each block of 16 queries: wave (kh, qw) takes keys
+  // [kh * 64 / KH, (kh + 1) * 64 / KH) of every 64-key tile with its own
+  // online-softmax state; the KH states are merged through LDS at the end.
+  static_assert(KH == 1 || KH == 2, "key halves");
+  constexpr int NWV = 4 * KH;                       // waves
+  constexpr int NKB = 4 / KH;                       // 16-key blocks per wave per tile
   constexpr int NKC = HD / 32, NCB = HD / 16;
   constexpr int KCH = HD / 8;                       // 16-byte chunks per K row
   constexpr int K_BYTES = kAttnKeys * HD * 2, V_BYTES = HD * kAttnKeys * 2;
   constexpr int STAGE = K_BYTES + V_BYTES;
   constexpr int K_INSTR = K_BYTES / 1024, V_INSTR = V_BYTES / 1024;
-  constexpr int IPW = (K_INSTR + V_INSTR) / 4;      // per wave
-  static_assert((K_INSTR + V_INSTR) % 4 == 0, "instructions per wave");
+  constexpr int IPW = (K_INSTR + V_INSTR) / NWV;    // per wave
+  static_assert((K_INSTR + V_INSTR) % NWV == 0, "instructions per wave");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qw = wave & 3, kh = wave >> 2;
   const int bg = blockIdx.y;
   const int b = bg / nkv, g = bg % nkv;
   const int G = nq / nkv;
   const int r0 = row_start[b], Mb = row_start[b + 1] - r0;
   const int Qn = Mb * G;
   const int qbase = blockIdx.x * kAttnQ;
-  if (qbase >= Qn) return;
+  if (qbase >= Qn) return;  // uniform over the workgroup
 
-  const int qv = qbase + wave * 16 + (lane & 15);
+  const int qv = qbase + qw * 16 + (lane & 15);
   const bool qok = qv < Qn;
-  const bool wave_live = qbase + wave * 16 < Qn;  // wave-uniform
+  const bool wave_live = qbase + qw * 16 < Qn;  // wave-uniform
   const int row = r0 + (qok ? qv / G : 0);
   const int head = g * G + (qok ? qv % G : 0);
   const size_t slab = ((size_t)b * nkv + g) * N * HD;
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
   int dst[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int j = wave + i * 4;
+    const int j = wave + i * NWV;
     if (j < K_INSTR) {
       const int kr = j * (1024 / (HD * 2)) + lane / KCH;       // key row in the tile
       const int lc = (lane % KCH) ^ kswz(kr, KCH);
@@ -316,7 +323,7 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
     unsigned char* st = smem + (t % STAGES) * STAGE;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int j = wave + i * 4;
+      const int j = wave + i * NWV;
       const size_t adv = j < K_INSTR ? (size_t)t * kAttnKeys * HD : (size_t)t * kAttnKeys;
       attn_dma16(src[i] + adv, st + dst[i]);
     }
@@ -345,6 +352,7 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
     }
   }
 
+  const int kofs = kh * (kAttnKeys / KH);  // first key of this wave in a tile
   for (int t = 0; t < ntiles; ++t) {
     // this wave's loads of tile t (later tiles may stay in flight), then
     // everyone's; every wave is done with tile t-1 after the barrier
@@ -353,11 +361,11 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
     if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1);
     if (!wave_live) continue;  // no query of this wave is valid: loads only
     const unsigned char* st = smem + (t % STAGES) * STAGE;
-    f32x4 s[4];
+    f32x4 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = kb * 16 + (lane & 15);
+      const int r = kofs + kb * 16 + (lane & 15);
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
         const int lc = c * 4 + (lane >> 4);
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
     // normalised result is the same either way.
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = xor16_max(mx);
@@ -388,9 +396,9 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
       m_run = m_new;
     }
     float psum = 0.f;
-    s16x4 pb[4];
+    s16x4 pb[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -406,13 +414,36 @@ __global__ __launch_bounds__(256) void attn_mfma_dma_kernel(
     for (int cb = 0; cb < NCB; ++cb) {
       const int vr = cb * 16 + (lane & 15);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int u = kb * 4 + (lane >> 4);  // 8-byte unit: 4 keys
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int u = (kofs + kb * 16) / 4 + (lane >> 4);  // 8-byte unit: 4 keys
         const s16x4 va = *(const s16x4*)(st + K_BYTES + vr * 128 +
                                           (((u >> 1) ^ vswz(vr)) << 4) + ((u & 1) << 3));
         oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kb], oacc[cb], 0, 0, 0);
       }
     }
+  }
+
+  if constexpr (KH == 2) {
+    // merge the second key half into the first: (m, l, o) of two disjoint
+    // key sets combine by the log-sum-exp rule
+    attn_lds_barrier();  // every wave is done with the tiles in LDS
+    constexpr int REG = NCB * 64 * 16 + 64 * 8;  // o fragments + (m, l) per lane
+    unsigned char* mine = smem + qw * REG;
+    if (kh == 1) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) ((f32x4*)mine)[cb * 64 + lane] = oacc[cb];
+      ((float2*)(mine + NCB * 64 * 16))[lane] = make_float2(m_run, l_run);
+    }
+    attn_lds_barrier();
+    if (kh == 1) return;
+    const float2 ml = ((const float2*)(mine + NCB * 64 * 16))[lane];
+    const float m = fmaxf(m_run, ml.x);
+    const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - m);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) oacc[cb] = oacc[cb] * a0 + ((const f32x4*)mine)[cb * 64 + lane] * a1;
+    l_run = l_run * a0 + ml.y * a1;
+    m_run = m;
   }
 
   if (!qok) return;
@@ -526,6 +557,7 @@ namespace {
 struct AttnPlan {
   bool mfma;
   int qtiles, splits, keys_per_split, stages;
+  int key_halves;  // waves per 16-query block, each over its share of every key tile
   size_t ws;
 };
 
@@ -538,8 +570,9 @@ constexpr size_t kAttnSplitCap = 64ull << 20;  // split-KV partials never exceed
 // M = 20 .. 1024 active rows and N = 512, 1024 keys (32 heads of 128), where
 // 2 stages beat 4 at every point and more splits lost to the combine pass.
 AttnPlan make_attn_plan_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits_in,
-                            int stages_in) {
+                            int stages_in, int kh_in) {
   AttnPlan p{};
+  p.key_halves = kh_in == 1 || kh_in == 2 ? kh_in : 2;
   p.mfma = dtype == kBF16 && (hd == 64 || hd == 128) && nq % nkv == 0;
   p.splits = 1;
   p.keys_per_split = N;
@@ -568,10 +601,10 @@ AttnPlan make_attn_plan_cfg(int dtype, int M, int B, int N, int nq, int nkv, int
 }
 
 AttnPlan make_attn_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd) {
-  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, 0, 0);
+  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, 0, 0, 0);
 }
 
-template <int HD, bool SPLIT, int STAGES>
+template <int HD, bool SPLIT, int STAGES, int KH>
 void launch_attn_dma(dim3 grid, const void* q, const int32_t* row_start, const void* kc,
                      const void* vc, void* o, int N, int nq, int nkv, int kps, int M, float* po,
                      float* pml, hipStream_t s) {
@@ -579,24 +612,29 @@ void launch_attn_dma(dim3 grid, const void* q, const int32_t* row_start, const v
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attn_mfma_dma_kernel<HD, SPLIT, STAGES>),
+        reinterpret_cast<const void*>(&attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  attn_mfma_dma_kernel<HD, SPLIT, STAGES><<<grid, 256, lds, s>>>(
+  attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH><<<grid, 256 * KH, lds, s>>>(
       (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq, nkv,
       kps, M, po, pml);
 }
 
 template <int HD, bool SPLIT>
-void launch_attn_kernel(dim3 grid, bool dma, int stages, const void* q, const int32_t* row_start,
+void launch_attn_kernel(dim3 grid, bool dma, int stages, int kh, const void* q,
+                        const int32_t* row_start,
                         const void* kc, const void* vc, void* o, int N, int nq, int nkv,
                         int kps, int M, float* po, float* pml, hipStream_t s) {
   if (dma) {
-    if (stages == 2)
-      launch_attn_dma<HD, SPLIT, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
+    if (stages == 2 && kh == 2)
+      launch_attn_dma<HD, SPLIT, 2, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
+    else if (stages == 2)
+      launch_attn_dma<HD, SPLIT, 2, 1>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
+    else if (kh == 2)
+      launch_attn_dma<HD, SPLIT, 4, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
     else
-      launch_attn_dma<HD, SPLIT, 4>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
+      launch_attn_dma<HD, SPLIT, 4, 1>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
   } else {
     attn_mfma_kernel<HD, SPLIT><<<grid, 256, 0, s>>>((const bf16_t*)q, row_start,
                                                      (const bf16_t*)kc, (const bf16_t*)vc,
@@ -613,7 +651,7 @@ hipError_t run_attn_mfma(const AttnPlan& p, int M, int B, int N, int nq, int nkv
   if (p.splits > 1) {
     float* po = (float*)ws;
     float* pml = po + (size_t)p.splits * M * nq * HD;
-    launch_attn_kernel<HD, true>(grid, dma, p.stages, q, row_start, kc, vc, o, N, nq, nkv,
+    launch_attn_kernel<HD, true>(grid, dma, p.stages, p.key_halves, q, row_start, kc, vc, o, N, nq, nkv,
                                  p.keys_per_split, M, po, pml, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -621,7 +659,7 @@ hipError_t run_attn_mfma(const AttnPlan& p, int M, int B, int N, int nq, int nkv
     const int gsz = (int)std::min<size_t>((total + 255) / 256, 8192);
     attn_combine_kernel<bf16_t><<<gsz, 256, 0, s>>>(po, pml, p.splits, M * nq, HD, (bf16_t*)o);
   } else {
-    launch_attn_kernel<HD, false>(grid, dma, p.stages, q, row_start, kc, vc, o, N, nq, nkv,
+    launch_attn_kernel<HD, false>(grid, dma, p.stages, p.key_halves, q, row_start, kc, vc, o, N, nq, nkv,
                                   p.keys_per_split, M, nullptr, nullptr, s);
   }
   return hipGetLastError();
@@ -636,9 +674,9 @@ size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int h
 hipError_t launch_attention_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd,
                                 const void* q, const int32_t* row_start, const void* kc,
                                 const void* vc, void* o, void* ws, size_t ws_bytes, int splits,
-                                int stages, hipStream_t s) {
+                                int stages, int key_halves, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  AttnPlan p = make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, stages);
+  AttnPlan p = make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, stages, key_halves);
   if (p.mfma && p.ws > ws_bytes) {
     p.splits = 1;
     p.keys_per_split = N;
@@ -664,11 +702,11 @@ hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int
                             const void* q, const int32_t* row_start, const void* kc,
                             const void* vc, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
   return launch_attention_cfg(dtype, M, B, N, nq, nkv, hd, q, row_start, kc, vc, o, ws, ws_bytes,
-                              0, 0, s);
+                              0, 0, 0, s);
 }
 
 size_t attention_cfg_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits) {
-  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, 0).ws;
+  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, 0, 0).ws;
 }
 
 }  // namespace dlm

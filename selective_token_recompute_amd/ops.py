@@ -144,8 +144,9 @@ def attention(q, row_start, kc, vc, nq, nkv, hd, o=None, ws=None):
     return o
 
 
-def attention_config(q, row_start, kc, vc, nq, nkv, hd, splits=0, stages=0, o=None):
-    """attention() with a forced split-KV count and LDS stage count (0: the plan's)."""
+def attention_config(q, row_start, kc, vc, nq, nkv, hd, splits=0, stages=0, key_halves=0, o=None):
+    """attention() with a forced split-KV count, LDS stage count and waves per
+    16-query block (0: the plan's)."""
     M = q.shape[0]
     B, _, N, _ = kc.shape
     dt = _dt(q)
@@ -154,7 +155,8 @@ def attention_config(q, row_start, kc, vc, nq, nkv, hd, splits=0, stages=0, o=No
     need = int(L.lib().dlm_op_attention_config_ws_bytes(dt, M, B, N, nq, nkv, hd, splits))
     ws = _ws_cache(max(need, 256), q.device)
     L.check(L.lib().dlm_op_attention_config(dt, M, B, N, nq, nkv, hd, _p(q), _p(row_start), _p(kc),
-                                            _p(vc), _p(o), splits, stages, _p(ws), ws.numel(),
+                                            _p(vc), _p(o), splits, stages, key_halves, _p(ws),
+                                            ws.numel(),
                                             _s()), "dlm_op_attention_config")
     return o
 

@@ -166,16 +166,17 @@ def test_attention_bf16_mfma(B, N, nq, nkv, hd, rows):
 
 @pytest.mark.parametrize("splits", [0, 1, 2, 3, 8, 64])
 @pytest.mark.parametrize("stages", [2, 4])
-def test_attention_forced_plans(splits, stages):
+@pytest.mark.parametrize("key_halves", [1, 2])
+def test_attention_forced_plans(splits, stages, key_halves):
     """Every split-KV count (including more splits than 64-key tiles, which
-    the plan clamps, and a count that leaves a short last range) and LDS
-    depth, with two sequences of ragged row counts and GQA, against the
-    oracle."""
+    the plan clamps, and a count that leaves a short last range), LDS depth
+    and number of waves per 16-query block, with two sequences of ragged row
+    counts and GQA, against the oracle."""
     B, N, nq, nkv, hd = 2, 320, 8, 2, 128
     q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, [37, 70], seed=11)
     o = ops.attention_config(_dev(q.reshape(len(rs), nq * hd)), torch.from_numpy(rst).to(DEV),
                              _dev(kc), _dev(vc.transpose(0, 1, 3, 2)), nq, nkv, hd,
-                             splits=splits, stages=stages)
+                             splits=splits, stages=stages, key_halves=key_halves)
     ref = oracle.unit_attention(q, rs, kc, vc).reshape(len(rs), nq * hd)
     err = np.abs(_f64(o) - ref)
     assert (err <= 1e-2 + 2.0 ** -7 * np.abs(ref)).all(), err.max()
