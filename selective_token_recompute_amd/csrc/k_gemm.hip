@@ -541,6 +541,7 @@ constexpr TileCfg kCfgs[] = {
     {192, 128, 2, 4, 4, 64},  // 29: 8 waves, 3 slices in flight
     {192, 128, 4, 1, 3, 64},  // 30: one head per wave, 2 slices in flight
     {192, 128, 4, 1, 4, 64},  // 31: one head per wave, 3 slices in flight
+    {128, 128, 4, 1, 2, 64},  // 32: one head per wave, two workgroups per CU
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr bool cfgs_fit_lds() {
@@ -698,7 +699,8 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
     case 28: return run_mfma<192, 128, 2, 4, 3, 64, EPI>(a, p, ep, ws, s);
     case 29: return run_mfma<192, 128, 2, 4, 4, 64, EPI>(a, p, ep, ws, s);
     case 30: return run_mfma<192, 128, 4, 1, 3, 64, EPI>(a, p, ep, ws, s);
-    default: return run_mfma<192, 128, 4, 1, 4, 64, EPI>(a, p, ep, ws, s);
+    case 31: return run_mfma<192, 128, 4, 1, 4, 64, EPI>(a, p, ep, ws, s);
+    default: return run_mfma<128, 128, 4, 1, 2, 64, EPI>(a, p, ep, ws, s);
   }
 }
 
@@ -760,7 +762,7 @@ int pick_qkv_cfg(int M) {
   if (M <= 128) return 16;
   if (M <= 192) return 15;
   if (M <= 256) return 16;
-  if (M <= 384) return 15;
+  if (M <= 384) return 32;
   return 17;
 }
 
