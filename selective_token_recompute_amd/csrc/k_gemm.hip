@@ -542,6 +542,8 @@ constexpr TileCfg kCfgs[] = {
     {192, 128, 4, 1, 3, 64},  // 30: one head per wave, 2 slices in flight
     {192, 128, 4, 1, 4, 64},  // 31: one head per wave, 3 slices in flight
     {128, 128, 4, 1, 2, 64},  // 32: one head per wave, two workgroups per CU
+    {192, 192, 4, 2, 2, 64},  // 33: 8 waves, 48x96 per wave
+    {192, 192, 2, 2, 2, 64},  // 34: 96x96 per wave
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr bool cfgs_fit_lds() {
@@ -575,7 +577,7 @@ int pick_cfg(int M, int N, bool dual) {
   static const int kBucket[] = {16, 32, 64, 128, 192, 256, 320, 384, 512};
   static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 28, 28, 8, 13};
   static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 9, 13};
-  static const int kDual[] = {1, 1, 1, 8, 5, 9, 12, 12, 13, 13};
+  static const int kDual[] = {1, 1, 1, 8, 5, 9, 33, 33, 13, 13};
   static const int kWide[] = {7, 7, 14, 10, 12, 13, 25, 25, 13, 13};
   int b = 0;
   while (b < 9 && M > kBucket[b]) ++b;
@@ -700,7 +702,9 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
     case 29: return run_mfma<192, 128, 2, 4, 4, 64, EPI>(a, p, ep, ws, s);
     case 30: return run_mfma<192, 128, 4, 1, 3, 64, EPI>(a, p, ep, ws, s);
     case 31: return run_mfma<192, 128, 4, 1, 4, 64, EPI>(a, p, ep, ws, s);
-    default: return run_mfma<128, 128, 4, 1, 2, 64, EPI>(a, p, ep, ws, s);
+    case 32: return run_mfma<128, 128, 4, 1, 2, 64, EPI>(a, p, ep, ws, s);
+    case 33: return run_mfma<192, 192, 4, 2, 2, 64, EPI>(a, p, ep, ws, s);
+    default: return run_mfma<192, 192, 2, 2, 2, 64, EPI>(a, p, ep, ws, s);
   }
 }
 
