@@ -51,6 +51,10 @@ MID_RUN = synth.RunShape(2, 192, 64, 32, 64)   # two sequences, 2 semi-AR blocks
 # sequences of different prompt content, two semi-AR blocks
 MID_G7 = synth.ModelShape(2, 896, 7, 1, 128, 2368, 4000, bf16=True)
 MID_G7_RUN = synth.RunShape(3, 160, 32, 32, 64)
+# the long-context schedule (N=4096, 1024 prompt + 3072 generated in 12
+# semi-AR blocks of 256, one step per block) at small width
+LONG_SMALL = synth.ModelShape(2, 256, 4, 4, 64, 512, 1000, bf16=True)
+LONG_SMALL_RUN = synth.RunShape(1, 4096, 1024, 12, 256)
 
 
 @pytest.mark.parametrize("shape", [MID, MID_GQA], ids=["mha", "gqa"])
@@ -68,6 +72,14 @@ def test_mid_bf16_group7_batched(setting):
     pr = synth.gen_prompts(MID_G7, MID_G7_RUN)
     reps = run_lockstep(MID_G7, W, MID_G7_RUN, synth.LOCK_SETTINGS[setting], pr)
     _report(f"mid-g7/{setting}", reps)
+
+
+@pytest.mark.parametrize("setting", ["scheduled"])
+def test_long_context_blocks(setting):
+    reps = run_lockstep(LONG_SMALL, synth.gen_weights(LONG_SMALL), LONG_SMALL_RUN,
+                        synth.LOCK_SETTINGS[setting], synth.gen_prompts(LONG_SMALL, LONG_SMALL_RUN))
+    _report(f"long-4096/{setting}", reps)
+    assert reps[0].m == LONG_SMALL_RUN.seq_len
 
 
 def test_tiny_bf16_generic_path():
