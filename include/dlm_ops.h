@@ -143,6 +143,29 @@ int dlm_op_vocab_stats(int32_t M, int32_t V, int32_t mask_id, int32_t kl_dir, in
                        int32_t* has_kl, float* lse_row, int32_t* err, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* LM head with the vocabulary statistics fused into its epilogue (bf16
+ * operands, K % 64 == 0; else DLM_E_UNSUPPORTED).  Computes, on the M
+ * compacted rows, z = A W^T (A bf16 [M][K], W bf16 [V][K]) stored as
+ * dlm_op_gemm's DLM_EPI_LOGITS stores it (row r at (row_seq[r], row_pos[r])
+ * of z_cur [batch][seq_len][V], mask column -inf), and the same per-row and
+ * per-position outputs as dlm_op_vocab_stats (SureLock page, §2 locking
+ * condition) without re-reading z_cur: each output tile folds its logits and
+ * the row's previous logits into online partial sums (maximum, sum of
+ * e^{z-max}, sum of e^{z-max}(z - z_prev), sum of q(z_prev - z)), one
+ * partial per row and column tile in ws, which a second kernel merges per
+ * row.  ws: at least dlm_op_lm_head_stats_ws_bytes(M, V, K, cfg) bytes of
+ * device memory (no initial contents needed).  cfg: -1 for the default tile
+ * plan, else a tile configuration index (tuning; DLM_E_UNSUPPORTED for a
+ * configuration the fused epilogue is not built for). */
+size_t dlm_op_lm_head_stats_ws_bytes(int32_t M, int32_t V, int32_t K, int32_t cfg);
+int dlm_op_lm_head_stats(int32_t M, int32_t V, int32_t K, const void* A, const void* W,
+                         float* z_cur, const int32_t* row_seq, const int32_t* row_pos,
+                         int32_t seq_len, int32_t mask_id, int32_t kl_dir, const float* z_prev,
+                         const float* lse_prev, int32_t* has_prev, float* lse_cur,
+                         int32_t* argmax, float* conf, float* kl, int32_t* has_kl,
+                         float* lse_row, int32_t* err, int32_t cfg, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* Commit + lock transition of one step (SlowFast page §1/§2: confidence-
  * ranked top-k unmasking in semi-autoregressive blocks; SureLock page §2:
  * KL lock test with confidence gate, permanent deactivation).  Per sequence:

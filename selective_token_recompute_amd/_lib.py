@@ -32,7 +32,8 @@ EXPORTS = [
     "dlm_op_rope_table", "dlm_op_rope_scatter",
     "dlm_op_attention_ws_bytes", "dlm_op_attention", "dlm_op_attention_config_ws_bytes",
     "dlm_op_attention_config", "dlm_op_vocab_ws_bytes",
-    "dlm_op_vocab_stats", "dlm_op_commit_lock",
+    "dlm_op_vocab_stats", "dlm_op_lm_head_stats_ws_bytes", "dlm_op_lm_head_stats",
+    "dlm_op_commit_lock",
 ]
 
 i32 = ctypes.c_int32
@@ -120,6 +121,10 @@ def lib() -> ctypes.CDLL:
         L.dlm_op_vocab_ws_bytes.restype = sz
         L.dlm_op_vocab_ws_bytes.argtypes = [i32, i32]
         L.dlm_op_vocab_stats.argtypes = [i32, i32, i32, i32, i32] + [vp] * 14 + [sz, vp]
+        L.dlm_op_lm_head_stats_ws_bytes.restype = sz
+        L.dlm_op_lm_head_stats_ws_bytes.argtypes = [i32] * 4
+        L.dlm_op_lm_head_stats.argtypes = ([i32] * 3 + [vp] * 5 + [i32] * 3 + [vp] * 10 +
+                                           [i32, vp, sz, vp])
         L.dlm_op_commit_lock.argtypes = ([i32] * 10 + [f32, f32, i32, i32] + [vp] * 11 + [vp])
         _lib = L
     return _lib

@@ -80,6 +80,7 @@ size_t max_ws(const dlm_model_desc& m, const dlm_run_desc& r) {
     w = std::max(w, attention_ws_bytes(m.dtype, M, r.batch, r.seq_len, m.n_heads,
                                        m.n_kv_heads, m.head_dim));
     w = std::max(w, vocab_ws_bytes(M, m.vocab));
+    w = std::max(w, gemm_logits_stats_bytes(m.dtype, M, m.vocab, m.d_model));
   }
   return w;
 }
@@ -432,6 +433,28 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out) {
     return launch_rmsnorm_resid(dt, M, d, m.rms_eps, hres, part, sp_res, h->fnorm, a, s);
   }));
   float* zc = h->at<float>(y.z[cur]);
+  if (gemm_logits_stats_fusable(dt, d) && gemm_logits_stats_preferred(M, V)) {
+    // LM head whose epilogue also folds the posterior statistics (with the
+    // previous step's logits) into one partial per row and column tile; a
+    // small pass merges them per row.
+    GemmArgs g{dt, kEpiLogitsStats, M, V, d, a, h->lm, nullptr, zc, row_seq, row_pos, N,
+               m.mask_id, nullptr, nullptr, nullptr, nullptr, 0, 0, h->at<float>(y.z[prv]),
+               h->at<float>(y.lse[prv]), h->at<int32_t>(y.has_prev), ws};
+    const double fl = 2.0 * M * (double)V * d;
+    const double by = V * (double)d * es + M * (double)d * es + M * (double)V * 8.0;
+    h->flops += fl;
+    TRY(timed(h, DLM_K_GEMM_LM_HEAD, by, fl, [&] { return launch_gemm_logits_stats(g, -1, s); }));
+    const int nparts = gemm_logits_stats_parts(M, V, -1);
+    TRY(timed(h, DLM_K_VOCAB_STATS, M * (double)nparts * kVocabPartBytes, 0.0, [&] {
+      return launch_vocab_merge_parts(M, nparts, N, r.kl_dir, row_seq, row_pos,
+                                      h->at<float>(y.lse[prv]), h->at<int32_t>(y.has_prev),
+                                      h->at<float>(y.lse[cur]), ws, h->at<int32_t>(y.argmax),
+                                      h->at<float>(y.conf), h->at<float>(y.kl),
+                                      h->at<int32_t>(y.has_kl), h->at<float>(y.lse_row), ctl + 1,
+                                      s);
+    }));
+    return DLM_OK;
+  }
   TRY(gemm(DLM_K_GEMM_LM_HEAD, kEpiLogits, V, d, a, h->lm, nullptr, zc, nullptr));
   TRY(timed(h, DLM_K_VOCAB_STATS, M * (double)V * 8.0, 0.0, [&] {
     return launch_vocab_stats(M, V, m.mask_id, r.kl_dir, N, row_seq, row_pos, zc,
@@ -755,6 +778,41 @@ int dlm_op_vocab_stats(int32_t M, int32_t V, int32_t mask_id, int32_t kl_dir, in
   return hip_status(launch_vocab_stats(M, V, mask_id, kl_dir, seq_len, row_seq, row_pos, z_cur,
                                        z_prev, lse_prev, has_prev, lse_cur, argmax, conf, kl,
                                        has_kl, lse_row, err, ws, ws_bytes, (hipStream_t)stream));
+}
+
+size_t dlm_op_lm_head_stats_ws_bytes(int32_t M, int32_t V, int32_t K, int32_t cfg) {
+  if (M < 0 || V < 2 || K < 1 || cfg >= gemm_num_configs()) return 0;
+  if (!gemm_logits_stats_fusable(kBF16, K) || M == 0) return 0;
+  return (size_t)M * gemm_logits_stats_parts(M, V, cfg) * kVocabPartBytes;
+}
+
+int dlm_op_lm_head_stats(int32_t M, int32_t V, int32_t K, const void* A, const void* W,
+                         float* z_cur, const int32_t* row_seq, const int32_t* row_pos,
+                         int32_t seq_len, int32_t mask_id, int32_t kl_dir, const float* z_prev,
+                         const float* lse_prev, int32_t* has_prev, float* lse_cur,
+                         int32_t* argmax, float* conf, float* kl, int32_t* has_kl,
+                         float* lse_row, int32_t* err, int32_t cfg, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (M < 0 || V < 2 || K < 1 || (kl_dir != 0 && kl_dir != 1) || seq_len < 1 ||
+      mask_id < 0 || mask_id >= V || cfg >= gemm_num_configs())
+    return DLM_E_INVALID;
+  if (!gemm_logits_stats_fusable(kBF16, K)) return DLM_E_UNSUPPORTED;
+  if (M == 0) return DLM_OK;
+  if (!A || !W || !z_cur || !row_seq || !row_pos || !z_prev || !lse_prev || !has_prev ||
+      !lse_cur || !argmax || !conf || !kl || !has_kl || !lse_row || !err || !ws)
+    return DLM_E_INVALID;
+  auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (!al16(A) || !al16(W)) return DLM_E_INVALID;
+  const int nparts = gemm_logits_stats_parts(M, V, cfg);
+  if ((size_t)M * nparts * kVocabPartBytes > ws_bytes) return DLM_E_SIZE;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g{kBF16, kEpiLogitsStats, M, V, K, A, W, nullptr, z_cur, row_seq, row_pos, seq_len,
+             mask_id, nullptr, nullptr, nullptr, nullptr, 0, 0, z_prev, lse_prev, has_prev, ws};
+  const hipError_t e = launch_gemm_logits_stats(g, cfg, s);
+  if (e != hipSuccess) return e == hipErrorInvalidValue ? DLM_E_UNSUPPORTED : DLM_E_HIP;
+  return hip_status(launch_vocab_merge_parts(M, nparts, seq_len, kl_dir, row_seq, row_pos,
+                                             lse_prev, has_prev, lse_cur, ws, argmax, conf, kl,
+                                             has_kl, lse_row, err, s));
 }
 
 int dlm_op_commit_lock(int32_t batch, int32_t seq_len, int32_t prompt_len, int32_t mask_id,

@@ -10,7 +10,10 @@
 namespace dlm {
 
 enum Dtype { kF32 = 0, kBF16 = 1 };
-enum Epi { kEpiStoreF32 = 0, kEpiResidAdd = 1, kEpiSwiglu = 2, kEpiLogits = 3, kEpiQKV = 4 };
+enum Epi {
+  kEpiStoreF32 = 0, kEpiResidAdd = 1, kEpiSwiglu = 2, kEpiLogits = 3, kEpiQKV = 4,
+  kEpiLogitsStats = 5  // logits as kEpiLogits plus per-(row, column tile) posterior partials
+};
 
 // ---- compaction -------------------------------------------------------------
 hipError_t launch_compact(const uint64_t* bits, int B, int N, int32_t* row_seq, int32_t* row_pos,
@@ -56,6 +59,14 @@ struct GemmArgs {
   void* kc;
   void* vc;
   int nq, nkv;
+  // kEpiLogitsStats only: previous-step logits [B][seq_len][N] and
+  // log-normaliser [B][seq_len], has_prev [B][seq_len] (read only), the
+  // partials out [M][gemm_logits_stats_parts()] (VocabPart; S1 and T1 both
+  // accumulated, so either KL direction can be finished from them).
+  const float* zprev;
+  const float* lse_prev;
+  const int32_t* has_prev;
+  void* parts;
 };
 size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K);
 hipError_t launch_gemm(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
@@ -72,6 +83,18 @@ int gemm_num_configs();
 bool gemm_qkv_fusable(int dtype, int M, int hd, int K);
 hipError_t launch_gemm_cfg(const GemmArgs& a, int cfg, int splits, void* ws, size_t ws_bytes,
                            hipStream_t s);
+// LM head with the posterior statistics in its epilogue (kEpiLogitsStats):
+// supported for bf16 with K % 64 == 0.  Partials per row (one per column
+// tile of the plan) and their bytes; the launch never splits K and does not
+// use ws.  cfg >= 0 forces a tile configuration (sweeps).
+constexpr size_t kVocabPartBytes = 20;  // one partial: m, s0, s1, t1 (float), argmax (int32)
+bool gemm_logits_stats_fusable(int dtype, int K);
+// Whether the fused form is the faster one at this M (else the LM head with
+// kEpiLogits followed by launch_vocab_stats).
+bool gemm_logits_stats_preferred(int M, int N);
+int gemm_logits_stats_parts(int M, int N, int cfg);
+size_t gemm_logits_stats_bytes(int dtype, int M, int N, int K);
+hipError_t launch_gemm_logits_stats(const GemmArgs& a, int cfg, hipStream_t s);
 
 // ---- attention -----------------------------------------------------------------
 size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd);
@@ -94,6 +117,14 @@ hipError_t launch_vocab_stats(int M, int V, int mask_id, int kl_dir, int N,
                               int32_t* has_prev, float* lse_cur, int32_t* argmax, float* conf,
                               float* kl, int32_t* has_kl, float* lse_row, int32_t* err,
                               void* ws, size_t ws_bytes, hipStream_t s);
+
+// Merges partials [M][nparts] (from kEpiLogitsStats) and finishes the rows
+// as launch_vocab_stats does.
+hipError_t launch_vocab_merge_parts(int M, int nparts, int N, int kl_dir, const int32_t* row_seq,
+                                    const int32_t* row_pos, const float* lse_prev,
+                                    int32_t* has_prev, float* lse_cur, const void* parts,
+                                    int32_t* argmax, float* conf, float* kl, int32_t* has_kl,
+                                    float* lse_row, int32_t* err, hipStream_t s);
 
 // ---- commit + lock -------------------------------------------------------------------
 struct LockArgs {

@@ -13,9 +13,15 @@
 // into the float residual stream (out-projection, down-projection), SwiGLU
 // over a gate/up pair of weight matrices (silu(A Wg^T) * (A Wu^T), stored in
 // the storage type), and logits scattered to each row's (seq, pos) slot with
-// the mask token's column forced to -inf.
+// the mask token's column forced to -inf; the last optionally also folds
+// each row's logits, with the row's previous-step logits, into the partial
+// posterior statistics (log-normaliser, argmax, confidence, KL) of its column
+// tile, so that no separate pass re-reads the current logits.
+#include <utility>
+
 #include "common.h"
 #include "internal.h"
+#include "vocab_part.h"
 
 namespace dlm {
 
@@ -32,6 +38,10 @@ struct EpiParams {
   bf16_t* kc;
   bf16_t* vc;
   int nq, nkv;
+  const float* zprev;
+  const float* lse_prev;
+  const int32_t* has_prev;
+  VocabPart* parts;
 };
 
 template <int EPI, typename T>
@@ -136,6 +146,22 @@ __device__ __forceinline__ void quad_round(const unsigned (&pk)[4], unsigned (&T
   const int s = (t - K) & 3;
 #pragma unroll
   for (int q = 0; q < 4; ++q) T[q] = (q == s) ? recv : T[q];
+}
+
+template <bool B, typename T>
+__device__ __forceinline__ T& pick(T& a, T& b) {
+  if constexpr (B) return b;
+  else return a;
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI, bool SPLIT>
@@ -367,6 +393,94 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
                     f2bf(acc[i][jt][qq]);
           }
         }
+      }
+    }
+  } else if constexpr (EPI == kEpiLogitsStats) {
+    // Logits stored as for kEpiLogits.  Per row: the lane folds its TN
+    // columns (increasing column order) into a partial, the 16 lanes that
+    // hold the row merge by xor shuffles, the WAVES_N waves of a tile row
+    // merge through LDS (in wave order); one partial per (row, column tile).
+    // The rows' (slot, has_prev, lse_prev) are staged in LDS once per tile,
+    // and the previous logits of row block i+1 are loaded while block i is
+    // folded.
+    struct RowMeta {
+      long long slot;
+      int hp;
+      float lsep;
+    };
+    static_assert(!SPLIT, "the statistics epilogue needs complete sums");
+    constexpr size_t kRedBytes = (size_t)BM * WAVES_N * sizeof(VocabPart);
+    static_assert(kRedBytes % 16 == 0, "row metadata alignment");
+    static_assert(kRedBytes + BM * sizeof(RowMeta) <= (size_t)STAGES * STAGE_BYTES,
+                  "statistics staging must fit the operand ring");
+    __syncthreads();  // every wave is done with the operand ring
+    VocabPart* red = (VocabPart*)smem;                // [BM][WAVES_N]
+    RowMeta* meta = (RowMeta*)(smem + kRedBytes);     // [BM]
+    for (int t = tid; t < BM; t += 64 * NW) {
+      const int rr = min(m0 + t, M - 1);
+      const size_t slot = (size_t)ep.row_seq[rr] * ep.seq_len + ep.row_pos[rr];
+      const int hp = ep.has_prev[slot];
+      meta[t] = RowMeta{(long long)slot, hp, hp ? ep.lse_prev[slot] : 0.f};
+    }
+    __syncthreads();
+    // previous logits of row block i (read whether or not the row has a
+    // previous posterior: every slot is valid memory, unused values ignored)
+    auto load_block = [&](auto I, float(&zp)[4][TN]) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float* prow = ep.zprev + (size_t)meta[wm * WM + i * 16 + rq + q].slot * N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + brow(j) + cl;
+          zp[q][j] = col < N ? prow[col] : 0.f;
+        }
+      }
+    };
+    float zpa[4][TN], zpb[4][TN];
+    load_block(std::integral_constant<int, 0>{}, zpa);
+    // one row block (16 rows) of the wave per call, expanded at compile time
+    // (a plain unrolled loop over the row blocks exceeds the unroller's size
+    // limit for the largest tiles, which would leave acc in scratch)
+    auto row_block = [&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      float(&cur)[4][TN] = pick<(i & 1) != 0>(zpa, zpb);
+      float(&nxt)[4][TN] = pick<(i & 1) == 0>(zpa, zpb);
+      if constexpr (i + 1 < TM) load_block(std::integral_constant<int, i + 1>{}, nxt);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rl = wm * WM + i * 16 + rq + q;
+        const int row = m0 + rl;
+        const RowMeta mt = meta[rl];
+        const bool hp = mt.hp != 0;
+        float* zrow = (float*)ep.C + (size_t)mt.slot * N;
+        VocabPart a = vpart_empty();
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + brow(j) + cl;
+          if (col < N) {
+            const float zv = (col == ep.mask_id) ? -INFINITY : acc[i][j][q];
+            if (row < M) zrow[col] = zv;
+            vpart_visit<2>(a, col, zv, cur[q][j], hp, mt.lsep, ep.mask_id);
+          }
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) a = vmerge(a, vpart_shfl_xor(a, o));
+        if (cl == 0) red[rl * WAVES_N + wn] = a;
+      }
+      // keep loads of later row blocks from being hoisted above this point
+      // (register pressure of the large tiles)
+      asm volatile("" ::: "memory");
+    };
+    static_for<TM>(row_block);
+    __syncthreads();
+    for (int t = tid; t < BM; t += 64 * NW) {
+      const int row = m0 + t;
+      if (row < M) {
+        VocabPart a = red[t * WAVES_N];
+#pragma unroll
+        for (int w = 1; w < WAVES_N; ++w) a = vmerge(a, red[t * WAVES_N + w]);
+        ep.parts[(size_t)row * tiles_n + nt] = a;
       }
     }
   } else if (SPLIT) {
@@ -630,24 +744,29 @@ hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hi
     const int threads = 64 * WAVES_M * WAVES_N;
     const size_t lds = (size_t)STAGES * (BM + BN) * BK * 2;
     float* partial = (float*)ws;
+    if constexpr (EPI == kEpiLogitsStats) {
+      if (p.splits > 1) return hipErrorInvalidValue;  // the epilogue needs complete sums
+    }
     if (p.splits > 1) {
-      static bool attr = false;
-      if (!attr) {
-        (void)hipFuncSetAttribute(
-            reinterpret_cast<const void*>(
-                &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        attr = true;
+      if constexpr (EPI != kEpiLogitsStats) {
+        static bool attr = false;
+        if (!attr) {
+          (void)hipFuncSetAttribute(
+              reinterpret_cast<const void*>(
+                  &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true>),
+              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          attr = true;
+        }
+        gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true>
+            <<<grid, threads, lds, s>>>((const bf16_t*)a.A, (const bf16_t*)a.W,
+                                        (const bf16_t*)a.W2, ep, a.K, p.k_per_split, p.tiles_m,
+                                        p.tiles_n, partial);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const size_t total = (size_t)a.M * a.N;
+        const int g = (int)std::min<size_t>((total + 255) / 256, 8192);
+        if (!p.defer_reduce) splitk_reduce_kernel<EPI, bf16_t><<<g, 256, 0, s>>>(partial, p.splits, ep);
       }
-      gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true>
-          <<<grid, threads, lds, s>>>((const bf16_t*)a.A, (const bf16_t*)a.W,
-                                      (const bf16_t*)a.W2, ep, a.K, p.k_per_split, p.tiles_m,
-                                      p.tiles_n, partial);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      const size_t total = (size_t)a.M * a.N;
-      const int g = (int)std::min<size_t>((total + 255) / 256, 8192);
-      if (!p.defer_reduce) splitk_reduce_kernel<EPI, bf16_t><<<g, 256, 0, s>>>(partial, p.splits, ep);
     } else {
       static bool attr = false;
       if (!attr) {
@@ -708,6 +827,28 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
   }
 }
 
+// The statistics epilogue is instantiated for every configuration pick_cfg
+// returns for a non-dual GEMM, plus tile 24 for sweeps.
+hipError_t dispatch_logits_stats(const GemmArgs& a, const Plan& p, EpiParams ep, hipStream_t s) {
+  constexpr int E = kEpiLogitsStats;
+  switch (p.cfg) {
+    case 1: return run_mfma<64, 128, 2, 2, 4, 64, E>(a, p, ep, nullptr, s);
+    case 5: return run_mfma<192, 128, 2, 2, 3, 64, E>(a, p, ep, nullptr, s);
+    case 6: return run_mfma<96, 128, 1, 4, 3, 64, E>(a, p, ep, nullptr, s);
+    case 7: return run_mfma<32, 64, 1, 4, 4, 64, E>(a, p, ep, nullptr, s);
+    case 8: return run_mfma<128, 128, 2, 4, 3, 64, E>(a, p, ep, nullptr, s);
+    case 9: return run_mfma<256, 128, 4, 2, 3, 64, E>(a, p, ep, nullptr, s);
+    case 10: return run_mfma<128, 256, 2, 4, 3, 64, E>(a, p, ep, nullptr, s);
+    case 12: return run_mfma<192, 128, 2, 2, 2, 64, E>(a, p, ep, nullptr, s);
+    case 13: return run_mfma<256, 256, 2, 4, 2, 64, E>(a, p, ep, nullptr, s);
+    case 14: return run_mfma<64, 64, 2, 2, 4, 64, E>(a, p, ep, nullptr, s);
+    case 24: return run_mfma<192, 256, 2, 4, 2, 64, E>(a, p, ep, nullptr, s);
+    case 25: return run_mfma<384, 128, 4, 2, 2, 64, E>(a, p, ep, nullptr, s);
+    case 28: return run_mfma<192, 128, 2, 4, 3, 64, E>(a, p, ep, nullptr, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int EPI>
 hipError_t run_generic(const GemmArgs& a, EpiParams ep, hipStream_t s) {
   dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
@@ -726,10 +867,15 @@ hipError_t dispatch_generic(const GemmArgs& a, EpiParams ep, hipStream_t s) {
   }
 }
 
+EpiParams epi_params(const GemmArgs& a) {
+  return EpiParams{a.C,  a.M,   a.N,  a.row_seq, a.row_pos, a.seq_len,  a.mask_id,
+                   a.rope, (bf16_t*)a.q, (bf16_t*)a.kc, (bf16_t*)a.vc, a.nq, a.nkv,
+                   a.zprev, a.lse_prev, a.has_prev, (VocabPart*)a.parts};
+}
+
 hipError_t launch_plan(const GemmArgs& a, Plan p, void* ws, size_t ws_bytes, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  EpiParams ep{a.C, a.M, a.N, a.row_seq, a.row_pos, a.seq_len, a.mask_id, a.rope,
-               (bf16_t*)a.q, (bf16_t*)a.kc, (bf16_t*)a.vc, a.nq, a.nkv};
+  EpiParams ep = epi_params(a);
   if (a.epi == kEpiQKV) {
     p.splits = 1;  // the fused epilogue needs complete sums
     p.k_per_split = a.K;
@@ -790,6 +936,54 @@ hipError_t launch_gemm_deferred(const GemmArgs& a, void* ws, size_t ws_bytes, hi
 }
 
 int gemm_num_configs() { return kNumCfgs; }
+
+bool gemm_logits_stats_fusable(int dtype, int K) {
+  return dtype == kBF16 && K % kBK == 0 && K >= kBK;
+}
+
+namespace {
+// Tile of the fused LM head by M: the 4-wave 192x128 tile (two workgroups per
+// CU, so one workgroup's epilogue overlaps the other's main loop) for
+// 256 < M <= 384, else the plain LM-head choice.
+int pick_logits_stats_cfg(int M, int N) {
+  if (M > 256 && M <= 384) return 12;
+  return pick_cfg(M, N, false);
+}
+
+Plan logits_stats_plan(int M, int N, int K, int cfg) {
+  Plan p = make_plan_cfg(kBF16, kEpiLogitsStats, M, N, K, cfg >= 0 ? cfg : pick_logits_stats_cfg(M, N));
+  p.splits = 1;  // the epilogue needs complete sums
+  p.k_per_split = K;
+  p.ws = 0;
+  return p;
+}
+}  // namespace
+
+// Measured at V = 126464, d = 4096 against the LM head followed by the
+// separate statistics kernel: in the fused form every workgroup reads the
+// previous logits in its epilogue at about the same time, with the MFMA units
+// idle, so it is ahead only where the GEMM is short of tiles or runs two
+// workgroups per CU: M <= 64 and 256 < M <= 384.
+bool gemm_logits_stats_preferred(int M, int N) {
+  (void)N;
+  return M <= 64 || (M > 256 && M <= 384);
+}
+
+int gemm_logits_stats_parts(int M, int N, int cfg) {
+  if (M <= 0 || (cfg >= kNumCfgs)) return 0;
+  return logits_stats_plan(M, N, kBK, cfg).tiles_n;
+}
+
+size_t gemm_logits_stats_bytes(int dtype, int M, int N, int K) {
+  if (!gemm_logits_stats_fusable(dtype, K) || M <= 0) return 0;
+  return (size_t)M * gemm_logits_stats_parts(M, N, -1) * sizeof(VocabPart);
+}
+
+hipError_t launch_gemm_logits_stats(const GemmArgs& a, int cfg, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  if (!gemm_logits_stats_fusable(a.dtype, a.K) || cfg >= kNumCfgs) return hipErrorInvalidValue;
+  return dispatch_logits_stats(a, logits_stats_plan(a.M, a.N, a.K, cfg), epi_params(a), s);
+}
 
 // Same GEMM with a forced tile configuration (for tuning sweeps); cfg < 0
 // uses the default plan.

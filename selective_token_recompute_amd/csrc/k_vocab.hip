@@ -10,37 +10,18 @@
 // One pass reads the current logits z and, where a previous posterior
 // exists, the previous logits z' (the engine keeps each position's logits of
 // the last step, double-buffered by step parity, plus that step's
-// log-normaliser lse').  With an online max m it accumulates
-//   S0 = sum e^{z-m},  S1 = sum e^{z-m} (z - z'),   (KL(p_t || p_{t-1}))
-//   T1 = sum q (z' - z), q = e^{z' - lse'}          (KL(p_{t-1} || p_t))
-// so that lse = m + log S0, conf = 1/S0 and
-//   KL(p_t || p_{t-1}) = S1/S0 - (lse - lse'),  KL(p_{t-1} || p_t) = T1 + lse - lse'.
-// The mask token's column is excluded (probability 0).  Rows are split over
-// several workgroups (chunks of the vocabulary); a second pass merges the
-// chunk partials per row.
+// log-normaliser lse') and folds them into the partial statistics of
+// vocab_part.h.  Rows are split over several workgroups (chunks of the
+// vocabulary); a second pass merges the chunk partials per row.  The LM-head
+// GEMM can instead produce the partials in its epilogue (one per row and
+// column tile); vocab_merge_parts_kernel merges those.
 #include "common.h"
 #include "internal.h"
+#include "vocab_part.h"
 
 namespace dlm {
 
-struct VPart {
-  float m, s0, s1, t1;
-  int am;
-};
-
-__device__ __forceinline__ VPart vmerge(VPart a, VPart b) {
-  VPart r;
-  r.m = fmaxf(a.m, b.m);
-  const float fa = (a.m == -INFINITY) ? 0.f : __expf(a.m - r.m);
-  const float fb = (b.m == -INFINITY) ? 0.f : __expf(b.m - r.m);
-  r.s0 = a.s0 * fa + b.s0 * fb;
-  r.s1 = a.s1 * fa + b.s1 * fb;
-  r.t1 = a.t1 + b.t1;
-  if (a.m > b.m) r.am = a.am;
-  else if (b.m > a.m) r.am = b.am;
-  else r.am = min(a.am, b.am);
-  return r;
-}
+typedef VocabPart VPart;
 
 constexpr int kVThreads = 256;
 
@@ -59,31 +40,9 @@ __global__ __launch_bounds__(kVThreads) void vocab_partial_kernel(
   const float lsep = hp ? lse_prev[slot] : 0.f;
   const int v0 = c * chunk, v1 = min(V, v0 + chunk);
 
-  VPart acc{-INFINITY, 0.f, 0.f, 0.f, 0x7fffffff};
+  VPart acc = vpart_empty();
   auto visit = [&](int v, float zv, float zpv) {
-    if (v == mask_id || zv == -INFINITY) {
-      if (KLDIR == 1 && hp && v != mask_id) {
-        const float q = __expf(zpv - lsep);
-        if (q > 0.f) acc.t1 += q * (zpv - zv);
-      }
-      return;
-    }
-    const float d = zv - zpv;
-    if (zv > acc.m) {
-      const float sc = (acc.m == -INFINITY) ? 0.f : __expf(acc.m - zv);
-      acc.s0 = acc.s0 * sc + 1.f;
-      if (KLDIR == 0) acc.s1 = acc.s1 * sc + (hp ? d : 0.f);
-      acc.m = zv;
-      acc.am = v;
-    } else {
-      const float e = __expf(zv - acc.m);
-      acc.s0 += e;
-      if (KLDIR == 0 && hp) acc.s1 += e * d;
-    }
-    if (KLDIR == 1 && hp) {
-      const float q = __expf(zpv - lsep);
-      if (q > 0.f) acc.t1 += q * (zpv - zv);
-    }
+    vpart_visit<KLDIR>(acc, v, zv, zpv, hp, lsep, mask_id);
   };
   // each thread visits its elements in increasing v, so a strict '>' keeps
   // the smallest index among equal maxima
@@ -108,15 +67,7 @@ __global__ __launch_bounds__(kVThreads) void vocab_partial_kernel(
   }
   // wave merge then cross-wave merge
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    VPart b;
-    b.m = __shfl_xor(acc.m, o, 64);
-    b.s0 = __shfl_xor(acc.s0, o, 64);
-    b.s1 = __shfl_xor(acc.s1, o, 64);
-    b.t1 = __shfl_xor(acc.t1, o, 64);
-    b.am = __shfl_xor(acc.am, o, 64);
-    acc = vmerge(acc, b);
-  }
+  for (int o = 32; o > 0; o >>= 1) acc = vmerge(acc, vpart_shfl_xor(acc, o));
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) red[w] = acc;
   __syncthreads();
@@ -127,21 +78,17 @@ __global__ __launch_bounds__(kVThreads) void vocab_partial_kernel(
   }
 }
 
-// One thread per row: merge chunk partials (in chunk order), finish the
-// statistics, record lse for the next step, latch non-finite results.
-__global__ void vocab_merge_kernel(int M, int nchunks, int N, int kl_dir,
-                                   const int32_t* __restrict__ row_seq,
-                                   const int32_t* __restrict__ row_pos,
-                                   const float* __restrict__ lse_prev,
-                                   int32_t* __restrict__ has_prev, float* __restrict__ lse_cur,
-                                   const VPart* __restrict__ part, int32_t* __restrict__ argmax,
-                                   float* __restrict__ conf, float* __restrict__ kl,
-                                   int32_t* __restrict__ has_kl, float* __restrict__ lse_row,
-                                   int32_t* __restrict__ err) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= M) return;
-  VPart t = part[(size_t)r * nchunks];
-  for (int c = 1; c < nchunks; ++c) t = vmerge(t, part[(size_t)r * nchunks + c]);
+// Finishes row r from its merged partial: statistics, lse recorded for the
+// next step, has_prev set, non-finite lse latched.
+__device__ __forceinline__ void finish_row(int r, const VPart& t, int N, int kl_dir,
+                                           const int32_t* __restrict__ row_seq,
+                                           const int32_t* __restrict__ row_pos,
+                                           const float* __restrict__ lse_prev,
+                                           int32_t* __restrict__ has_prev,
+                                           float* __restrict__ lse_cur,
+                                           int32_t* __restrict__ argmax, float* __restrict__ conf,
+                                           float* __restrict__ kl, int32_t* __restrict__ has_kl,
+                                           float* __restrict__ lse_row, int32_t* __restrict__ err) {
   const size_t slot = (size_t)row_seq[r] * N + row_pos[r];
   const float lse = t.m + logf(t.s0);
   const bool hp = has_prev[slot] != 0;
@@ -159,6 +106,44 @@ __global__ void vocab_merge_kernel(int M, int nchunks, int N, int kl_dir,
   lse_cur[slot] = lse;
   has_prev[slot] = 1;
   if (!isfinite(lse)) atomicExch(err, 1);
+}
+
+// One thread per row: merge chunk partials (in chunk order), then finish.
+__global__ void vocab_merge_kernel(int M, int nchunks, int N, int kl_dir,
+                                   const int32_t* __restrict__ row_seq,
+                                   const int32_t* __restrict__ row_pos,
+                                   const float* __restrict__ lse_prev,
+                                   int32_t* __restrict__ has_prev, float* __restrict__ lse_cur,
+                                   const VPart* __restrict__ part, int32_t* __restrict__ argmax,
+                                   float* __restrict__ conf, float* __restrict__ kl,
+                                   int32_t* __restrict__ has_kl, float* __restrict__ lse_row,
+                                   int32_t* __restrict__ err) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= M) return;
+  VPart t = part[(size_t)r * nchunks];
+  for (int c = 1; c < nchunks; ++c) t = vmerge(t, part[(size_t)r * nchunks + c]);
+  finish_row(r, t, N, kl_dir, row_seq, row_pos, lse_prev, has_prev, lse_cur, argmax, conf, kl,
+             has_kl, lse_row, err);
+}
+
+// One wave per row over many partials [M][nparts]: lane l merges partials
+// l, l+64, ... in order, then the lanes merge by xor shuffles.
+__global__ __launch_bounds__(256) void vocab_merge_parts_kernel(
+    int M, int nparts, int N, int kl_dir, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, const float* __restrict__ lse_prev,
+    int32_t* __restrict__ has_prev, float* __restrict__ lse_cur, const VPart* __restrict__ part,
+    int32_t* __restrict__ argmax, float* __restrict__ conf, float* __restrict__ kl,
+    int32_t* __restrict__ has_kl, float* __restrict__ lse_row, int32_t* __restrict__ err) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= M) return;  // wave-uniform
+  VPart t = vpart_empty();
+  const VPart* p = part + (size_t)r * nparts;
+  for (int c = lane; c < nparts; c += 64) t = vmerge(t, p[c]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) t = vmerge(t, vpart_shfl_xor(t, o));
+  if (lane == 0)
+    finish_row(r, t, N, kl_dir, row_seq, row_pos, lse_prev, has_prev, lse_cur, argmax, conf, kl,
+               has_kl, lse_row, err);
 }
 
 namespace {
@@ -203,6 +188,19 @@ hipError_t launch_vocab_stats(int M, int V, int mask_id, int kl_dir, int N,
   vocab_merge_kernel<<<(M + 127) / 128, 128, 0, s>>>(M, p.chunks, N, kl_dir, row_seq, row_pos,
                                                       lse_prev, has_prev, lse_cur, part, argmax,
                                                       conf, kl, has_kl, lse_row, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_vocab_merge_parts(int M, int nparts, int N, int kl_dir, const int32_t* row_seq,
+                                    const int32_t* row_pos, const float* lse_prev,
+                                    int32_t* has_prev, float* lse_cur, const void* parts,
+                                    int32_t* argmax, float* conf, float* kl, int32_t* has_kl,
+                                    float* lse_row, int32_t* err, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  vocab_merge_parts_kernel<<<(M + 3) / 4, 256, 0, s>>>(M, nparts, N, kl_dir, row_seq, row_pos,
+                                                      lse_prev, has_prev, lse_cur,
+                                                      (const VPart*)parts, argmax, conf, kl,
+                                                      has_kl, lse_row, err);
   return hipGetLastError();
 }
 

@@ -185,6 +185,32 @@ def vocab_stats(row_seq, row_pos, z_cur, z_prev, lse_prev, has_prev, lse_cur, ma
     return out
 
 
+def lm_head_stats(A, W, z_cur, row_seq, row_pos, z_prev, lse_prev, has_prev, lse_cur, mask_id,
+                  kl_dir=0, cfg=-1):
+    """LM head (bf16 A [M][K] x W [V][K]) storing logits into z_cur [B][N][V]
+    at each row's (seq, pos) slot, with the vocabulary statistics computed in
+    its epilogue; returns the same dict as vocab_stats()."""
+    M, K = A.shape
+    V = W.shape[0]
+    B, N, _ = z_cur.shape
+    dev = A.device
+    out = dict(argmax=torch.empty(M, dtype=torch.int32, device=dev),
+               conf=torch.empty(M, dtype=torch.float32, device=dev),
+               kl=torch.empty(M, dtype=torch.float32, device=dev),
+               has_kl=torch.empty(M, dtype=torch.int32, device=dev),
+               lse=torch.empty(M, dtype=torch.float32, device=dev),
+               err=torch.zeros(1, dtype=torch.int32, device=dev))
+    need = int(L.lib().dlm_op_lm_head_stats_ws_bytes(M, V, K, cfg))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    L.check(L.lib().dlm_op_lm_head_stats(M, V, K, _p(A), _p(W), _p(z_cur), _p(row_seq),
+                                         _p(row_pos), N, mask_id, kl_dir, _p(z_prev),
+                                         _p(lse_prev), _p(has_prev), _p(lse_cur),
+                                         _p(out["argmax"]), _p(out["conf"]), _p(out["kl"]),
+                                         _p(out["has_kl"]), _p(out["lse"]), _p(out["err"]), cfg,
+                                         _p(ws), ws.numel(), _s()), "dlm_op_lm_head_stats")
+    return out
+
+
 def commit_lock(*, batch, seq_len, prompt_len, mask_id, blk_lo, blk_hi, k, do_commit, do_lock,
                 policy, kl_eps, conf_tau, n_consec, lock_prompt, row_seq, row_pos, row_start,
                 row_real, argmax, conf, kl, has_kl, tokens, bits, counters):

@@ -257,6 +257,130 @@ def test_vocab_stats_adversarial():
     assert np.abs(g["kl"]).max() <= 2e-6
 
 
+# --- LM head with the statistics in its epilogue ------------------------------------------
+
+LMSTATS_CFGS = [1, 5, 6, 7, 8, 9, 10, 12, 13, 14, 24, 25, 28]  # tiles the fused epilogue is built for
+
+
+def _lm_head_stats_case(M, V, K, kl_dir, cfg=-1, seed=0, A=None, W=None):
+    """Runs the fused LM head on M rows scattered over B=2 sequences of 96
+    positions; returns (GPU outputs, the GPU's stored logits of the rows, the
+    oracle's logits, the oracle's statistics of the GPU's logits, context)."""
+    B, N = 2, 96
+    rng = np.random.default_rng(seed)
+    flat = np.sort(rng.choice(B * N, M, replace=False))
+    rs, rp = (flat // N).astype(np.int32), (flat % N).astype(np.int32)
+    if A is None:
+        A, W, _ = _gemm_inputs(M, V, K, seed=seed + 11)
+    zref = oracle.unit_linear(A, W)
+    zprev = (rng.standard_normal((B, N, V)) * 0.3).astype(np.float32)
+    zprev[rs, rp] = (zref + rng.standard_normal((M, V)) * 0.05).astype(np.float32)
+    zprev[..., V - 1] = -np.inf
+    lse_prev = oracle.unit_vocab_stats(zprev.reshape(-1, V), mask_id=V - 1)["lse"]
+    lse_prev = lse_prev.astype(np.float32).reshape(B, N)
+    hp = (rng.random((B, N)) < 0.7).astype(np.int32)
+    Z = torch.full((B, N, V), 7.0, device=DEV)
+    hp_d = torch.from_numpy(hp.copy()).to(DEV)
+    lse_cur = torch.full((B, N), -5.0, device=DEV)
+    out = ops.lm_head_stats(_dev(A), _dev(W), Z, torch.from_numpy(rs).to(DEV),
+                            torch.from_numpy(rp).to(DEV), torch.from_numpy(zprev).to(DEV),
+                            torch.from_numpy(lse_prev).to(DEV), hp_d, lse_cur, mask_id=V - 1,
+                            kl_dir=kl_dir, cfg=cfg)
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    z = Z.cpu().numpy()
+    got = z[rs, rp]
+    prev_logp = zprev[rs, rp].astype(np.float64) - lse_prev[rs, rp].astype(np.float64)[:, None]
+    ref = oracle.unit_vocab_stats(got, prev_logp, hp[rs, rp].astype(np.uint8), mask_id=V - 1,
+                                  kl_dir=kl_dir)
+    ctx = dict(rs=rs, rp=rp, z=z, hp=hp, hp_after=hp_d.cpu().numpy(),
+               lse_cur=lse_cur.cpu().numpy(), zprev=zprev, lse_prev=lse_prev)
+    return g, got, zref, ref, ctx
+
+
+def _check_lm_head_stats(g, got, zref, ref, ctx, V):
+    rs, rp = ctx["rs"], ctx["rp"]
+    # the logits: stored at each row's slot, mask column -inf, other slots untouched
+    assert np.isneginf(got[:, V - 1]).all()
+    assert np.abs(got[:, :-1] - zref[:, :-1]).max() <= 1e-5 * max(1, np.abs(zref).max())
+    untouched = np.ones(ctx["z"].shape[:2], bool)
+    untouched[rs, rp] = False
+    assert (ctx["z"][untouched] == 7.0).all()
+    # the statistics of those logits
+    hk = ctx["hp"][rs, rp].astype(bool)
+    assert np.array_equal(g["argmax"], ref["argmax"])
+    assert np.allclose(g["conf"], ref["conf"], rtol=1e-5, atol=0)
+    assert np.allclose(g["lse"], ref["lse"], rtol=0, atol=2e-5)
+    assert np.array_equal(g["has_kl"].astype(bool), hk)
+    assert np.isnan(g["kl"][~hk]).all()
+    if hk.any():
+        assert np.allclose(g["kl"][hk], ref["kl"][hk], rtol=1e-3, atol=2e-6), \
+            np.abs(g["kl"][hk] - ref["kl"][hk]).max()
+    # per-position state: has_prev set and lse recorded at the active slots only
+    after = ctx["hp"].copy()
+    after[rs, rp] = 1
+    assert np.array_equal(ctx["hp_after"], after)
+    assert np.allclose(ctx["lse_cur"][rs, rp], ref["lse"], atol=2e-5)
+    assert (ctx["lse_cur"][untouched] == -5.0).all()
+    assert g["err"][0] == 0
+
+
+@pytest.mark.parametrize("M,V,K", [(1, 1000, 256), (37, 1001, 256), (150, 9001, 128),
+                                   (192, 40000, 128), (100, 126464, 64)])
+@pytest.mark.parametrize("kl_dir", [0, 1])
+def test_lm_head_stats_vs_oracle(M, V, K, kl_dir):
+    g, got, zref, ref, ctx = _lm_head_stats_case(M, V, K, kl_dir, seed=M + V + kl_dir)
+    _check_lm_head_stats(g, got, zref, ref, ctx, V)
+
+
+@pytest.mark.parametrize("cfg", LMSTATS_CFGS)
+def test_lm_head_stats_every_tile(cfg):
+    g, got, zref, ref, ctx = _lm_head_stats_case(70, 1001, 128, cfg % 2, cfg=cfg, seed=cfg)
+    _check_lm_head_stats(g, got, zref, ref, ctx, 1001)
+
+
+def test_lm_head_stats_matches_unfused_path():
+    """Same logits and statistics as the LM-head GEMM followed by the separate
+    vocabulary-statistics kernel."""
+    M, V, K = 120, 5000, 256
+    g, got, zref, ref, ctx = _lm_head_stats_case(M, V, K, 0, seed=5)
+    rs, rp = (torch.from_numpy(ctx[k]).to(DEV) for k in ("rs", "rp"))
+    A, W, _ = _gemm_inputs(M, V, K, seed=5 + 11)
+    Z = torch.full((2, 96, V), 7.0, device=DEV)
+    ops.gemm(L.DLM_EPI_LOGITS, _dev(A), _dev(W), C=Z, row_seq=rs, row_pos=rp, seq_len=96,
+             mask_id=V - 1)
+    assert np.array_equal(Z.cpu().numpy(), ctx["z"])  # identical logits, bit for bit
+    zprev = torch.from_numpy(ctx["zprev"]).to(DEV)
+    lse_prev = torch.from_numpy(ctx["lse_prev"]).to(DEV)
+    u = ops.vocab_stats(rs, rp, Z, zprev, lse_prev,
+                        torch.from_numpy(ctx["hp"].copy()).to(DEV), torch.zeros((2, 96), device=DEV),
+                        mask_id=V - 1, kl_dir=0)
+    u = {k: v.cpu().numpy() for k, v in u.items()}
+    assert np.array_equal(u["argmax"], g["argmax"])
+    assert np.allclose(u["conf"], g["conf"], rtol=1e-5)
+    assert np.allclose(u["lse"], g["lse"], atol=1e-5)
+    hk = u["has_kl"].astype(bool)
+    assert np.array_equal(hk, g["has_kl"].astype(bool))
+    assert np.allclose(u["kl"][hk], g["kl"][hk], rtol=1e-3, atol=2e-6)
+
+
+def test_lm_head_stats_ties_and_mask_column():
+    """Equal maxima in different column tiles go to the smaller index; a
+    mask-token column with the largest logit never counts."""
+    M, V, K = 40, 3000, 128
+    A, W, _ = _gemm_inputs(M, V, K, seed=77)
+    A[:, 0] = 1.0
+    row = W[5].copy()
+    row[0] = 4.0
+    W[5] = row      # three equal winners in different column tiles
+    W[700] = row
+    W[2998] = row
+    W[V - 1, 0] = 40.0  # the mask column: largest, excluded
+    g, got, zref, ref, ctx = _lm_head_stats_case(M, V, K, 0, seed=3, A=A, W=W)
+    assert (got[:, 5] == got[:, 700]).all() and (got[:, 5] == got[:, 2998]).all()
+    assert (g["argmax"] == 5).all()
+    _check_lm_head_stats(g, got, zref, ref, ctx, V)
+
+
 # --- commit + lock (bit exact) ----------------------------------------------------
 
 def _golden():
