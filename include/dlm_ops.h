@@ -125,6 +125,22 @@ int dlm_op_attention_config(int32_t dtype, int32_t M, int32_t batch, int32_t seq
                             int32_t stages, int32_t key_halves, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* QKV projection with the rotary embedding and the K/V cache scatter in the
+ * GEMM epilogue (SureLock page, §2: fresh Q/K/V only for the active rows,
+ * K/V of every position kept in the cache), as dlm_step runs it for bf16
+ * models with head_dim 128: A bf16 [M][K] (K % 64 == 0, else
+ * DLM_E_UNSUPPORTED), W bf16 [(nq + 2 nkv) 128][K] (q heads, k heads, v
+ * heads).  Row r (sequence row_seq[r], position row_pos[r]) writes q bf16
+ * [M][nq 128] rotated, K cache bf16 [batch][nkv][seq_len][128] rotated and
+ * the transposed V cache bf16 [batch][nkv][128][seq_len]; rope_table as
+ * dlm_op_rope_table writes it (null: no rotation).  cfg: -1 for the default
+ * tile plan, else a tile configuration with 128-column tiles (else
+ * DLM_E_UNSUPPORTED). */
+int dlm_op_gemm_qkv(int32_t M, int32_t K, int32_t nq, int32_t nkv, int32_t seq_len,
+                    const void* A, const void* W, const int32_t* row_seq, const int32_t* row_pos,
+                    const float* rope_table, void* q, void* kcache, void* vcache, int32_t cfg,
+                    void* stream);
+
 /* Vocabulary statistics of the active rows (SureLock page, §2 locking
  * condition: KL between the current and previous posterior, confidence
  * gate).  Logits live per position: z_cur/z_prev float [batch][seq_len][V],

@@ -29,7 +29,7 @@ EXPORTS = [
     "dlm_last_step_info", "dlm_destroy", "dlm_error_string", "dlm_set_timing",
     "dlm_read_timing", "dlm_op_compact", "dlm_op_embed_rmsnorm", "dlm_op_rmsnorm",
     "dlm_op_gemm_ws_bytes", "dlm_op_gemm", "dlm_op_gemm_num_configs", "dlm_op_gemm_config",
-    "dlm_op_rope_table", "dlm_op_rope_scatter",
+    "dlm_op_gemm_qkv", "dlm_op_rope_table", "dlm_op_rope_scatter",
     "dlm_op_attention_ws_bytes", "dlm_op_attention", "dlm_op_attention_config_ws_bytes",
     "dlm_op_attention_config", "dlm_op_vocab_ws_bytes",
     "dlm_op_vocab_stats", "dlm_op_lm_head_stats_ws_bytes", "dlm_op_lm_head_stats",
@@ -109,6 +109,7 @@ def lib() -> ctypes.CDLL:
                                   sz, vp]
         L.dlm_op_gemm_config.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32,
                                          i32, i32, vp, sz, vp]
+        L.dlm_op_gemm_qkv.argtypes = [i32] * 5 + [vp] * 8 + [i32, vp]
         L.dlm_op_rope_table.argtypes = [i32, i32, f32, vp, vp]
         L.dlm_op_rope_scatter.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                           vp, vp]

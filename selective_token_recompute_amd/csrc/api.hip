@@ -694,6 +694,27 @@ int dlm_op_gemm_config(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t
   return hip_status(launch_gemm_cfg(g, cfg, splits, ws, ws ? ws_bytes : 0, (hipStream_t)stream));
 }
 
+int dlm_op_gemm_qkv(int32_t M, int32_t K, int32_t nq, int32_t nkv, int32_t seq_len,
+                    const void* A, const void* W, const int32_t* row_seq, const int32_t* row_pos,
+                    const float* rope_table, void* q, void* kcache, void* vcache, int32_t cfg,
+                    void* stream) {
+  if (M < 0 || K < 1 || nq < 1 || nkv < 1 || nq % nkv || seq_len < 1 ||
+      cfg >= gemm_num_configs())
+    return DLM_E_INVALID;
+  if (K % 64 != 0) return DLM_E_UNSUPPORTED;
+  if (M == 0) return DLM_OK;
+  if (!A || !W || !row_seq || !row_pos || !q || !kcache || !vcache) return DLM_E_INVALID;
+  auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (!al16(A) || !al16(W) || ((uintptr_t)q & 3) || ((uintptr_t)kcache & 3) ||
+      ((uintptr_t)vcache & 7) || (rope_table && !al16(rope_table)))
+    return DLM_E_INVALID;
+  GemmArgs g{kBF16, kEpiQKV, M, (nq + 2 * nkv) * 128, K, A, W, nullptr, nullptr, row_seq, row_pos,
+             seq_len, 0, rope_table, q, kcache, vcache, nq, nkv};
+  const hipError_t e = launch_gemm_cfg(g, cfg, 1, nullptr, 0, (hipStream_t)stream);
+  if (e == hipErrorInvalidValue) return DLM_E_UNSUPPORTED;
+  return hip_status(e);
+}
+
 int dlm_op_rope_table(int32_t seq_len, int32_t head_dim, float base, float* table,
                       void* stream) {
   if (seq_len < 1 || head_dim < 2 || (head_dim & 1) || !table || !(base > 0.f))

@@ -79,7 +79,7 @@ hipError_t launch_gemm_deferred(const GemmArgs& a, void* ws, size_t ws_bytes, hi
 int gemm_num_configs();
 // QKV projection with rotary embedding and K/V cache scatter fused into the
 // epilogue (bf16, head_dim 128, K % 64 == 0); false if the shape is not
-// supported (then use kEpiStoreF32 + launch_rope_scatter).
+// supported (then use kEpiStoreF32 + launch_rope_scatter_split).
 bool gemm_qkv_fusable(int dtype, int M, int hd, int K);
 hipError_t launch_gemm_cfg(const GemmArgs& a, int cfg, int splits, void* ws, size_t ws_bytes,
                            hipStream_t s);

@@ -129,23 +129,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T>
-__device__ __forceinline__ T sel4(const T (&a)[4], int i) {
-  return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
-}
-
-// One round of a 4x4 transpose within lane quads: lane t sends pk[(t+K)&3],
-// and the value received from lane (t-K)&3 (DPP quad_perm CTRL) is that
-// lane's column for row t, stored at T[(t-K)&3].  Before the first round
-// T[t] = pk[t]; after rounds 1..3, T[s] = (row t, column 4*(quad)+s).
-template <int K, int CTRL>
-__device__ __forceinline__ void quad_round(const unsigned (&pk)[4], unsigned (&T)[4], int t) {
-  const unsigned send = sel4(pk, (t + K) & 3);
-  const unsigned recv =
-      (unsigned)__builtin_amdgcn_update_dpp(0, (int)send, CTRL, 0xf, 0xf, false);
-  const int s = (t - K) & 3;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) T[q] = (q == s) ? recv : T[q];
+// Largest divisor k of waves_m such that k wave rows of wm tile rows, of
+// row_bytes each, fit in ring bytes (0 if none does).
+constexpr int qkv_wave_rows_per_pass(int waves_m, int wm, int row_bytes, int ring) {
+  for (int k = waves_m; k >= 1; --k)
+    if (waves_m % k == 0 && (long long)k * wm * row_bytes <= ring) return k;
+  return 0;
 }
 
 template <bool B, typename T>
@@ -302,99 +291,103 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
   // epilogue
   const int rq = (lane >> 4) * 4, cl = lane & 15;
   if constexpr (EPI == kEpiQKV) {
-    // The tile is one head (BN = hd = 128) and each wave holds all of its
-    // columns, so lane l has both halves (c, c + 64) of each rotary pair.
-    static_assert(BN == 128 && WAVES_N == 1, "fused QKV epilogue needs one head per wave");
+    // The tile is one head (BN = hd = 128).  The fp32 tile is staged in LDS
+    // (the operand ring is free by now), with each row's (sequence,
+    // position), in passes of whole wave rows when it does not fit at once,
+    // so that any thread can pair column c with c + 64 for the rotary
+    // embedding and the stores coalesce: q and K rows as packed bf16 pairs
+    // along the head dimension, V transposed with 4 consecutive positions per
+    // 8-byte store.  The item loops have compile-time trip counts and are
+    // unrolled so that their loads are all in flight together.
+    static_assert(BN == 128, "the fused QKV epilogue needs one head per tile");
+    constexpr int LDW = 132;  // padded LDS row stride (floats)
+    constexpr int NT = 64 * NW;
+    constexpr int WMP = qkv_wave_rows_per_pass(WAVES_M, WM, LDW * 4 + 8, STAGES * STAGE_BYTES);
+    static_assert(WMP >= 1, "one wave row of the tile must fit the LDS ring");
+    constexpr int PR = WMP * WM;  // tile rows per pass
+    static_assert(PR % 4 == 0, "row quads");
+    float* T = (float*)smem;
+    int2* meta = (int2*)(smem + (size_t)PR * LDW * 4);  // (sequence, position) per row
     const int hix = n0 / 128;  // head in the q | k | v list
     const int nq = ep.nq, nkv = ep.nkv, Nseq = ep.seq_len;
+    auto pass = [&](auto P) __attribute__((always_inline)) {
+      constexpr int p = decltype(P)::value;
+      const int r0 = m0 + p * PR;  // first row of this pass
+      __syncthreads();  // operand ring, or the previous pass's rows, no longer read
+      if (wm / WMP == p) {
+        const int rb = (wm % WMP) * WM;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      int rows[4], seqs[4], poss[4];
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        rows[qq] = m0 + wm * WM + i * 16 + rq + qq;
-        const int rr = min(rows[qq], M - 1);
-        seqs[qq] = ep.row_seq[rr];
-        poss[qq] = ep.row_pos[rr];
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              T[(rb + i * 16 + rq + q) * LDW + wn * WN + j * 16 + cl] = acc[i][j][q];
       }
+      for (int r = tid; r < PR; r += NT) {
+        const int rr = min(r0 + r, M - 1);
+        meta[r] = make_int2(ep.row_seq[rr], ep.row_pos[rr]);
+      }
+      __syncthreads();
       if (hix < nq + nkv) {
-        // all rotary factors of this row block first (independent loads in
-        // flight together), then the rotations and stores
-        float cs[4][4], sn[4][4];
+        // q or K head: item = (row, two consecutive rotary pairs jp, jp + 1)
+        constexpr int ITEMS = PR * 32, ITER = (ITEMS + NT - 1) / NT;
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const float2 t2 = ep.rope ? *(const float2*)(ep.rope +
-                                                         ((size_t)poss[qq] * 64 + jt * 16 + cl) * 2)
-                                      : make_float2(1.f, 0.f);
-            cs[jt][qq] = t2.x;
-            sn[jt][qq] = t2.y;
-          }
-        // 4x4 transpose inside each quad of lanes (DPP quad permutes) so that
-        // lane t of a quad holds row rq+t at 4 consecutive columns: one
-        // 8-byte store per half-head instead of four 2-byte stores
-        const int t = cl & 3, c4 = cl & ~3;
-        const int row_t = sel4(rows, t);
-        bf16_t* dst = hix < nq ? ep.q + (size_t)row_t * nq * 128 + (size_t)hix * 128
-                               : ep.kc + (((size_t)sel4(seqs, t) * nkv + (hix - nq)) * Nseq +
-                                          sel4(poss, t)) * 128;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          // rotary pair (c, c + 64), c = jt * 16 + cl; low half c, high half c + 64
-          unsigned pk[4];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const float a0 = acc[i][jt][qq], a1 = acc[i][jt + 4][qq];
-            const float r0 = a0 * cs[jt][qq] - a1 * sn[jt][qq];
-            const float r1 = a0 * sn[jt][qq] + a1 * cs[jt][qq];
-            pk[qq] = (unsigned)f2bf(r0) | ((unsigned)f2bf(r1) << 16);
-          }
-          unsigned T[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) T[q] = pk[q];  // T[t] = pk[t] is the k = 0 round
-          quad_round<1, 0x93>(pk, T, t);
-          quad_round<2, 0x4e>(pk, T, t);
-          quad_round<3, 0x39>(pk, T, t);
-          if (row_t < M) {
-            ushort4 lo, hi;
-            lo.x = (unsigned short)(T[0] & 0xffff);
-            lo.y = (unsigned short)(T[1] & 0xffff);
-            lo.z = (unsigned short)(T[2] & 0xffff);
-            lo.w = (unsigned short)(T[3] & 0xffff);
-            hi.x = (unsigned short)(T[0] >> 16);
-            hi.y = (unsigned short)(T[1] >> 16);
-            hi.z = (unsigned short)(T[2] >> 16);
-            hi.w = (unsigned short)(T[3] >> 16);
-            *(ushort4*)(dst + jt * 16 + c4) = lo;
-            *(ushort4*)(dst + 64 + jt * 16 + c4) = hi;
+        for (int k = 0; k < ITER; ++k) {
+          const int it = tid + k * NT;
+          const int r = it >> 5, jp = (it & 31) * 2;
+          const int row = r0 + r;
+          if (it < ITEMS && row < M) {
+            const int2 sp = meta[r];
+            const float2 lo = *(const float2*)(T + r * LDW + jp);
+            const float2 hi = *(const float2*)(T + r * LDW + 64 + jp);
+            const float4 cs = ep.rope ? *(const float4*)(ep.rope + ((size_t)sp.y * 64 + jp) * 2)
+                                      : make_float4(1.f, 0.f, 1.f, 0.f);
+            bf16_t* dst = hix < nq ? ep.q + (size_t)row * nq * 128 + (size_t)hix * 128
+                                   : ep.kc + (((size_t)sp.x * nkv + (hix - nq)) * Nseq + sp.y) *
+                                                 128;
+            *(uint32_t*)(dst + jp) = f2bf2(lo.x * cs.x - hi.x * cs.y, lo.y * cs.z - hi.y * cs.w);
+            *(uint32_t*)(dst + 64 + jp) =
+                f2bf2(lo.x * cs.y + hi.x * cs.x, lo.y * cs.w + hi.y * cs.z);
           }
         }
       } else {
+        // V head, stored transposed: item = (row quad, column c)
         const int g = hix - nq - nkv;
-        const bool packed = rows[3] < M && seqs[3] == seqs[0] && poss[3] == poss[0] + 3 &&
-                            seqs[1] == seqs[0] && poss[1] == poss[0] + 1 &&
-                            seqs[2] == seqs[0] && poss[2] == poss[0] + 2 && (poss[0] & 3) == 0;
+        constexpr int ITEMS = (PR / 4) * 128, ITER = (ITEMS + NT - 1) / NT;
 #pragma unroll
-        for (int jt = 0; jt < 8; ++jt) {
-          const int c = jt * 16 + cl;
-          if (packed) {
-            ushort4 w;
-            w.x = f2bf(acc[i][jt][0]);
-            w.y = f2bf(acc[i][jt][1]);
-            w.z = f2bf(acc[i][jt][2]);
-            w.w = f2bf(acc[i][jt][3]);
-            *(ushort4*)(ep.vc + (((size_t)seqs[0] * nkv + g) * 128 + c) * Nseq + poss[0]) = w;
-          } else {
+        for (int k = 0; k < ITER; ++k) {
+          const int it = tid + k * NT;
+          const int c = it & 127, r4 = (it >> 7) * 4;
+          const int row = r0 + r4;
+          if (it < ITEMS && row < M) {
+            int2 sp[4];
+            float v[4];
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq)
-              if (rows[qq] < M)
-                ep.vc[(((size_t)seqs[qq] * nkv + g) * 128 + c) * Nseq + poss[qq]] =
-                    f2bf(acc[i][jt][qq]);
+            for (int t = 0; t < 4; ++t) {
+              sp[t] = meta[r4 + t];
+              v[t] = T[(r4 + t) * LDW + c];
+            }
+            const bool packed = row + 3 < M && (Nseq & 3) == 0 && (sp[0].y & 3) == 0 &&
+                                sp[3].x == sp[0].x && sp[3].y == sp[0].y + 3 &&
+                                sp[1].x == sp[0].x && sp[1].y == sp[0].y + 1 &&
+                                sp[2].x == sp[0].x && sp[2].y == sp[0].y + 2;
+            if (packed) {
+              uint2 w;
+              w.x = f2bf2(v[0], v[1]);
+              w.y = f2bf2(v[2], v[3]);
+              *(uint2*)(ep.vc + (((size_t)sp[0].x * nkv + g) * 128 + c) * Nseq + sp[0].y) = w;
+            } else {
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                if (row + t < M)
+                  ep.vc[(((size_t)sp[t].x * nkv + g) * 128 + c) * Nseq + sp[t].y] = f2bf(v[t]);
+            }
           }
         }
       }
-    }
+    };
+    static_for<WAVES_M / WMP>(pass);
   } else if constexpr (EPI == kEpiLogitsStats) {
     // Logits stored as for kEpiLogits.  Per row: the lane folds its TN
     // columns (increasing column order) into a partial, the 16 lanes that
@@ -737,8 +730,8 @@ hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hi
   constexpr bool DUAL = EPI == kEpiSwiglu;
   if constexpr (DUAL && ((BN / WAVES_N / 16) % 2 != 0)) {
     return hipErrorInvalidValue;  // a dual tile needs matching gate/up column tiles per wave
-  } else if constexpr (EPI == kEpiQKV && !(BN == 128 && WAVES_N == 1)) {
-    return hipErrorInvalidValue;  // the fused QKV epilogue needs one head per wave
+  } else if constexpr (EPI == kEpiQKV && BN != 128) {
+    return hipErrorInvalidValue;  // the fused QKV epilogue needs one head per tile
   } else {
     dim3 grid(p.tiles_m * p.tiles_n, p.splits, 1);
     const int threads = 64 * WAVES_M * WAVES_N;
@@ -904,16 +897,19 @@ size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K) {
 }
 
 bool gemm_qkv_fusable(int dtype, int M, int hd, int K) {
-  return dtype == kBF16 && hd == 128 && K % kBK == 0 && M >= 96;
+  return dtype == kBF16 && hd == 128 && K % kBK == 0 && M >= 1;
 }
 
-// Tile for the fused QKV epilogue by M.
+// Tile for the fused QKV epilogue by M, from a sweep of every 128-column
+// configuration at the LLaDA-8B shape (d 4096 -> 12288); at every M it beat
+// the plain GEMM followed by the separate rotary / scatter kernels.
 int pick_qkv_cfg(int M) {
-  if (M <= 128) return 16;
-  if (M <= 192) return 15;
-  if (M <= 256) return 16;
-  if (M <= 384) return 32;
-  return 17;
+  if (M <= 64) return 0;    // 32x128, 4 waves: weight streaming
+  if (M <= 128) return 1;   // 64x128
+  if (M <= 192) return 6;   // 96x128
+  if (M <= 256) return 8;   // 128x128, 8 waves
+  if (M <= 384) return 28;  // 192x128, 8 waves
+  return 9;                 // 256x128, 8 waves
 }
 
 hipError_t launch_gemm(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {

@@ -114,6 +114,15 @@ def num_gemm_configs() -> int:
     return int(L.lib().dlm_op_gemm_num_configs())
 
 
+def gemm_qkv(A, W, row_seq, row_pos, table, q, kc, vc, nq, nkv, cfg=-1):
+    """QKV projection with rotary embedding and cache scatter fused (bf16,
+    head_dim 128): q [M][nq*128], kc [B][nkv][N][128], vc [B][nkv][128][N]."""
+    M, K = A.shape
+    L.check(L.lib().dlm_op_gemm_qkv(M, K, nq, nkv, kc.shape[2], _p(A), _p(W), _p(row_seq),
+                                    _p(row_pos), _p(table), _p(q), _p(kc), _p(vc), cfg, _s()),
+            "dlm_op_gemm_qkv")
+
+
 def rope_table(seq_len: int, head_dim: int, base: float, device="cuda") -> torch.Tensor:
     t = torch.empty((seq_len, head_dim // 2, 2), dtype=torch.float32, device=device)
     L.check(L.lib().dlm_op_rope_table(seq_len, head_dim, float(base), _p(t), _s()),

@@ -523,6 +523,62 @@ def test_rope_scatter(bf16):
     assert (np.moveaxis(vcn, 3, 2)[np.broadcast_to(~touched[:, None, :], kcn.shape[:3])] == 3.0).all()
 
 
+QKV_CFGS = [0, 1, 2, 4, 5, 6, 8, 9, 11, 12, 15, 16, 17, 18, 19, 21, 22, 23, 25, 28, 29, 30, 31,
+            32]  # every tile configuration with 128-column (one-head) tiles
+
+
+def _qkv_fused_case(M, N, cfg, seed):
+    """Fused QKV (projection + rotary + cache scatter) on M rows of B=2
+    sequences of N positions, GQA 4/2 heads of 128; returns the GPU outputs
+    and the oracle's (fp64 linear, rotary)."""
+    B, nq, nkv, hd, K = 2, 4, 2, 128, 256
+    rng = np.random.default_rng(seed)
+    flat = np.sort(rng.choice(B * N, M, replace=False))
+    rs, rp = (flat // N).astype(np.int32), (flat % N).astype(np.int32)
+    A, W, _ = _gemm_inputs(M, (nq + 2 * nkv) * hd, K, seed=seed + 1)
+    table = ops.rope_table(N, hd, 10000.0)
+    q = torch.zeros((M, nq * hd), dtype=torch.bfloat16, device=DEV)
+    kc = torch.full((B, nkv, N, hd), 3.0, dtype=torch.bfloat16, device=DEV)
+    vc = torch.full((B, nkv, hd, N), 3.0, dtype=torch.bfloat16, device=DEV)
+    ops.gemm_qkv(_dev(A), _dev(W), torch.from_numpy(rs).to(DEV), torch.from_numpy(rp).to(DEV),
+                 table, q, kc, vc, nq, nkv, cfg=cfg)
+    x = oracle.unit_linear(A, W).reshape(M, nq + 2 * nkv, hd)
+    rot = oracle.unit_rope(x[:, : nq + nkv], rp, 10000.0)
+    return dict(rs=rs, rp=rp, q=_f64(q), kc=_f64(kc), vc=_f64(vc), x=x, rot=rot, nq=nq, nkv=nkv)
+
+
+def _check_qkv_fused(c, B=2):
+    tol = lambda ref: 2.0 ** -8 * np.abs(ref) + 1e-5
+    nq, nkv, rs, rp = c["nq"], c["nkv"], c["rs"], c["rp"]
+    M = len(rs)
+    qr = c["rot"][:, :nq].reshape(M, -1)
+    assert (np.abs(c["q"] - qr) <= tol(qr)).all(), np.abs(c["q"] - qr).max()
+    kr = c["rot"][:, nq:]                      # [M][nkv][hd]
+    kg = c["kc"][rs, :, rp]                    # [M][nkv][hd]
+    assert (np.abs(kg - kr) <= tol(kr)).all(), np.abs(kg - kr).max()
+    vr = c["x"][:, nq + nkv:]
+    vg = np.moveaxis(c["vc"], 3, 2)[rs, :, rp]  # [M][nkv][hd]
+    assert (np.abs(vg - vr) <= tol(vr)).all(), np.abs(vg - vr).max()
+    N = c["kc"].shape[2]
+    untouched = np.ones((B, N), bool)
+    untouched[rs, rp] = False
+    assert (np.moveaxis(c["kc"], 2, 1)[untouched] == 3.0).all()
+    assert (np.moveaxis(c["vc"], 3, 1)[untouched] == 3.0).all()
+
+
+@pytest.mark.parametrize("cfg", QKV_CFGS)
+def test_gemm_qkv_fused_every_tile(cfg):
+    # dense active rows (runs of consecutive positions: packed V stores) and
+    # a ragged row count
+    _check_qkv_fused(_qkv_fused_case(203, 128, cfg, seed=cfg))
+
+
+@pytest.mark.parametrize("M,N", [(1, 600), (37, 602), (96, 130), (384, 512), (500, 4096)])
+def test_gemm_qkv_fused_default_plan(M, N):
+    # N % 4 != 0 takes the unpacked V stores; sparse rows break position runs
+    _check_qkv_fused(_qkv_fused_case(M, N, -1, seed=M + N))
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("epi", [L.DLM_EPI_STORE_F32, L.DLM_EPI_RESID_ADD, L.DLM_EPI_SWIGLU,
                                  L.DLM_EPI_LOGITS])
