@@ -108,7 +108,8 @@ def roofline_entry(tim, setting_ms):
 
 
 TRAFFIC_SOURCES = ("selective_token_recompute_amd/csrc/k_gemm.hip",
-                   "selective_token_recompute_amd/csrc/common.h")
+                   "selective_token_recompute_amd/csrc/common.h",
+                   "selective_token_recompute_amd/csrc/vocab_part.h")
 
 
 def sources_sha256(paths=TRAFFIC_SOURCES):
@@ -328,6 +329,8 @@ def main():
     ap.add_argument("--extra-steps", type=int, default=16)
     ap.add_argument("--full-runs", action="store_true",
                     help="time whole runs of the extra configurations")
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="extra timed regions of the configured setting (spread only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 1 GiB device copies (counter calibration for profiles)")
     args = ap.parse_args()
@@ -361,6 +364,10 @@ def main():
         log(f"[{s}] {K} steps in {dt * 1e3:.1f} ms -> {K / dt:.1f} steps/s, "
             f"{toks / dt:.1f} tokens/s, mean M {sum(ms) / len(ms):.1f}")
         results[s] = dict(seconds=dt, tokens=toks, ms=ms)
+
+    # the configured setting's timed region again, for its run-to-run spread
+    spread = [K / nat_dt for nat_dt in (run_steps(factory("natural"), K)[0]
+                                        for _ in range(args.repeats))]
 
     # per-kernel event timing over the same steps (configured setting)
     _, _, ms_nat, tim = run_steps(factory("natural"), K, timing=True)
@@ -397,6 +404,9 @@ def main():
                                "masked), 128-step runs, lock: KL<=1e-3 & max-prob>=0.9 x2",
                    "global_batch": run.batch, "seq_len": run.seq_len, "parallelism": "none"},
         "mean_active_rows": round(sum(nat["ms"]) / len(nat["ms"]), 1),
+        "repeats": dict(steps_per_s=[round(v, 3) for v in spread],
+                        note="the same K timed steps run again after the timed region "
+                             "(not part of value)"),
         "roofline": roof,
         "kernels": kernels,
     }
