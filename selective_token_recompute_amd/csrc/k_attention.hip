@@ -279,12 +279,20 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qw = wave & 3, kh = wave >> 2;
-  const int bg = blockIdx.y;
+  // XCD-aware order: workgroup i (x fastest) runs on XCD i % 8; give
+  // consecutive workgroups of one XCD the query tiles of one (sequence,
+  // kv head), which then read its K/V slab through that XCD's L2.
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int total = nx * ny * gridDim.z;
+  int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  const int bx = lin % nx, by = (lin / nx) % ny, bz = lin / (nx * ny);
+  const int bg = by;
   const int b = bg / nkv, g = bg % nkv;
   const int G = nq / nkv;
   const int r0 = row_start[b], Mb = row_start[b + 1] - r0;
   const int Qn = Mb * G;
-  const int qbase = blockIdx.x * kAttnQ;
+  const int qbase = bx * kAttnQ;
   if (qbase >= Qn) return;  // uniform over the workgroup
 
   const int qv = qbase + qw * 16 + (lane & 15);
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
   const size_t slab = ((size_t)b * nkv + g) * N * HD;
   const bf16_t* kslab = kc + slab;  // [N][HD]
   const bf16_t* vslab = vc + slab;  // [HD][N]
-  const int key0 = blockIdx.z * keys_per_split;
+  const int key0 = bz * keys_per_split;
   const int key1 = min(N, key0 + keys_per_split);
   const int ntiles = key1 > key0 ? (key1 - key0) / kAttnKeys : 0;
   const float scale = kLog2e / sqrtf((float)HD);
@@ -449,7 +457,7 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
   if (!qok) return;
   const int gq = row * nq + head;
   if (SPLIT) {
-    const size_t base = (size_t)blockIdx.z * M * nq + gq;
+    const size_t base = (size_t)bz * M * nq + gq;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
       *(f32x4*)(part_o + base * HD + cb * 16 + (lane >> 4) * 4) = oacc[cb];
