@@ -51,9 +51,30 @@ __global__ __launch_bounds__(kVThreads) void vocab_partial_kernel(
     const int n4 = (v1 - v0) >> 2;
     const float4* z4 = (const float4*)(z + v0);
     const float4* zp4 = (const float4*)(zp + v0);
-    for (int i = threadIdx.x; i < n4; i += kVThreads) {
+    // U float4 of z (and of z') loaded before any is folded, so that the
+    // loads of a thread are in flight together
+    constexpr int U = 4;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    int i = threadIdx.x;
+    for (; i + (U - 1) * kVThreads < n4; i += U * kVThreads) {
+      float4 a[U], p[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a[u] = z4[i + u * kVThreads];
+        p[u] = hp ? zp4[i + u * kVThreads] : zero;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + 4 * (i + u * kVThreads);
+        visit(v, a[u].x, p[u].x);
+        visit(v + 1, a[u].y, p[u].y);
+        visit(v + 2, a[u].z, p[u].z);
+        visit(v + 3, a[u].w, p[u].w);
+      }
+    }
+    for (; i < n4; i += kVThreads) {
       const float4 a = z4[i];
-      const float4 p = hp ? zp4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 p = hp ? zp4[i] : zero;
       const int v = v0 + 4 * i;
       visit(v, a.x, p.x);
       visit(v + 1, a.y, p.y);
@@ -106,24 +127,6 @@ __device__ __forceinline__ void finish_row(int r, const VPart& t, int N, int kl_
   lse_cur[slot] = lse;
   has_prev[slot] = 1;
   if (!isfinite(lse)) atomicExch(err, 1);
-}
-
-// One thread per row: merge chunk partials (in chunk order), then finish.
-__global__ void vocab_merge_kernel(int M, int nchunks, int N, int kl_dir,
-                                   const int32_t* __restrict__ row_seq,
-                                   const int32_t* __restrict__ row_pos,
-                                   const float* __restrict__ lse_prev,
-                                   int32_t* __restrict__ has_prev, float* __restrict__ lse_cur,
-                                   const VPart* __restrict__ part, int32_t* __restrict__ argmax,
-                                   float* __restrict__ conf, float* __restrict__ kl,
-                                   int32_t* __restrict__ has_kl, float* __restrict__ lse_row,
-                                   int32_t* __restrict__ err) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= M) return;
-  VPart t = part[(size_t)r * nchunks];
-  for (int c = 1; c < nchunks; ++c) t = vmerge(t, part[(size_t)r * nchunks + c]);
-  finish_row(r, t, N, kl_dir, row_seq, row_pos, lse_prev, has_prev, lse_cur, argmax, conf, kl,
-             has_kl, lse_row, err);
 }
 
 // One wave per row over many partials [M][nparts]: lane l merges partials
@@ -185,7 +188,9 @@ hipError_t launch_vocab_stats(int M, int V, int mask_id, int kl_dir, int N,
                                                        z_cur, z_prev, lse_prev, has_prev, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  vocab_merge_kernel<<<(M + 127) / 128, 128, 0, s>>>(M, p.chunks, N, kl_dir, row_seq, row_pos,
+  // one wave per row: the chunk partials of a row are loaded in parallel
+  // (a thread per row walking them in order waits one load latency per chunk)
+  vocab_merge_parts_kernel<<<(M + 3) / 4, 256, 0, s>>>(M, p.chunks, N, kl_dir, row_seq, row_pos,
                                                       lse_prev, has_prev, lse_cur, part, argmax,
                                                       conf, kl, has_kl, lse_row, err);
   return hipGetLastError();
