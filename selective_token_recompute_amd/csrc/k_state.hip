@@ -156,6 +156,7 @@ __global__ __launch_bounds__(kLockThreads) void commit_lock_kernel(LockArgs a) {
       const float cf = cconf[c];
       const int cp = cpos[c];
       int rank = 0;
+#pragma unroll 8
       for (int j = 0; j < C; ++j) {
         const float f = cconf[j];
         rank += (f > cf) || (f == cf && cpos[j] < cp);
