@@ -121,6 +121,11 @@ __device__ __forceinline__ void wait_slices(int n) {
   }
 }
 
+// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt at their maxima).
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
 // Workgroup barrier without the vmcnt(0) that __syncthreads() implies; the
 // empty asm statements keep the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -153,7 +158,8 @@ __device__ __forceinline__ void static_for(F& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI, bool SPLIT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI, bool SPLIT,
+          bool PF = false>
 __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, const bf16_t* __restrict__ W2,
     EpiParams ep, int K, int k_per_split, int tiles_m, int tiles_n, float* __restrict__ partial) {
@@ -274,18 +280,94 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
           acc[i][j] =
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(F.a[ks][i], F.b[ks][j], acc[i][j], 0, 0, 0);
   };
-  // slice kt: publish it, refill the slot of slice kt-1 (every wave has
-  // passed this barrier, so it finished slice kt-1), then read and multiply
+  if constexpr (!PF) {
+    // slice kt: publish it, refill the slot of slice kt-1 (every wave has
+    // passed this barrier, so it finished slice kt-1), then read and multiply
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s);
-  for (int kt = 0; kt < KT; ++kt) {
-    wait_slices<IPW, STAGES - 1>(min(STAGES - 2, KT - 1 - kt));
-    lds_barrier();
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-    Frags f;
-    read_frags(kt, f);
-    mma(f);
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KT) issue(s);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_slices<IPW, STAGES - 1>(min(STAGES - 2, KT - 1 - kt));
+      lds_barrier();
+      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+      Frags f;
+      read_frags(kt, f);
+      mma(f);
+      {
+        // issue order within the slice: the first k-step's fragment reads,
+        // then its MFMAs interleaved with the next k-step's reads, then the
+        // remaining MFMAs (the compiler's own order waited for most reads
+        // before the first MFMA; measured 1-6% faster)
+        constexpr int R = TM + TN, MM = TM * TN;
+        constexpr int PER = MM / R > 0 ? MM / R : 1;
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, KS * MM - (KS - 1) * R * PER, 0);
+      }
+    }
+  } else {
+    // Fragment prefetch over a 3-slot ring: while the MFMAs of slice kt run
+    // on fragments already in registers, the fragments of slice kt+1 are
+    // read from LDS, and slice kt+3 is loaded into the slot slice kt left
+    // (every wave read it before this step's barrier).  Two slices of loads
+    // are in flight behind the one being read.
+    static_assert(STAGES == 3, "fragment prefetch runs a 3-slot ring");
+    static_assert(2 * IPW < 64, "in-flight loads must fit the vmcnt counter");
+    constexpr int RT = (TM + TN) * KS, MT = TM * TN * KS;
+    constexpr int PER = MT / RT > 0 ? MT / RT : 1;
+    Frags f0, f1;
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      if (s < KT) issue(s);
+    if (KT > 0) {
+      wait_slices<IPW, 3>(min(2, KT - 1));
+      lds_barrier();
+      read_frags(0, f0);
+      wait_lgkm0();
+    }
+    // steady step: slice kt+1 lands, slice kt+3 is issued (kt + 3 < KT)
+    auto step = [&](int kt, Frags& cur, Frags& nxt) __attribute__((always_inline)) {
+      wait_slices<IPW, 3>(1);
+      lds_barrier();
+      issue(kt + 3);
+      read_frags(kt + 1, nxt);
+      mma(cur);
+      __builtin_amdgcn_sched_group_barrier(0x010, IPW, 0);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MT - RT * PER, 0);
+      wait_lgkm0();  // this wave's reads of slot kt+1 are done before the next barrier
+    };
+    // last steps: nothing more to issue, no read after the last slice
+    auto tail = [&](int kt, Frags& cur, Frags& nxt) __attribute__((always_inline)) {
+      if (kt + 1 < KT) {
+        wait_slices<IPW, 3>(min(1, max(0, KT - 2 - kt)));
+        lds_barrier();
+        if (kt + 3 < KT) issue(kt + 3);
+        read_frags(kt + 1, nxt);
+      }
+      mma(cur);
+      wait_lgkm0();
+    };
+    int kt = 0;
+    for (; kt + 4 < KT; kt += 2) {
+      step(kt, f0, f1);
+      step(kt + 1, f1, f0);
+    }
+    for (; kt < KT; kt += 2) {
+      tail(kt, f0, f1);
+      if (kt + 1 < KT) tail(kt + 1, f1, f0);
+    }
   }
 
   // epilogue
@@ -614,6 +696,7 @@ namespace {
 
 struct TileCfg {
   int bm, bn, wm, wn, stages, bk;
+  bool pf = false;  // fragment prefetch over a 3-slot ring
 };
 constexpr TileCfg kCfgs[] = {
     {32, 128, 1, 4, 4, 64},   // 0: weight streaming
@@ -651,6 +734,11 @@ constexpr TileCfg kCfgs[] = {
     {128, 128, 4, 1, 2, 64},  // 32: one head per wave, two workgroups per CU
     {192, 192, 4, 2, 2, 64},  // 33: 8 waves, 48x96 per wave
     {192, 192, 2, 2, 2, 64},  // 34: 96x96 per wave
+    {192, 192, 4, 2, 3, 64, true},  // 35: 33 with fragment prefetch
+    {192, 128, 2, 4, 3, 64, true},  // 36: 28 with fragment prefetch
+    {256, 128, 4, 2, 3, 64, true},  // 37: 9 with fragment prefetch
+    {128, 128, 2, 4, 3, 64, true},  // 38: 8 with fragment prefetch
+    {128, 256, 2, 4, 3, 64, true},  // 39: 10 with fragment prefetch
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr bool cfgs_fit_lds() {
@@ -676,15 +764,15 @@ struct Plan {
 // configurations on MI355X at the LLaDA-8B shapes (QKV 4096->12288, O
 // 4096->4096, gate/up 4096->2x12288, down 12288->4096, LM head
 // 4096->126464) with the weights streamed from HBM: small M favours narrow
-// row tiles that stream the weights with many workgroups; around M = 384 the
-// gate/up and QKV projections favour 2-stage 4-wave tiles with two
-// workgroups per CU, the O / down projections and the LM head 8-wave tiles;
-// large M favours 256x256 tiles with 8 waves.
+// row tiles that stream the weights with many workgroups; from M ~ 192 to
+// 512, 8-wave tiles with fragment prefetch that give every CU one workgroup
+// (gate/up 192x192 at M = 384: 2 x 128 tiles); large M favours 256x256
+// tiles with 8 waves.
 int pick_cfg(int M, int N, bool dual) {
   static const int kBucket[] = {16, 32, 64, 128, 192, 256, 320, 384, 512};
-  static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 28, 28, 8, 13};
-  static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 9, 13};
-  static const int kDual[] = {1, 1, 1, 8, 5, 9, 33, 33, 13, 13};
+  static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 36, 36, 8, 13};
+  static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 37, 13};
+  static const int kDual[] = {1, 1, 1, 8, 5, 37, 35, 35, 13, 13};
   static const int kWide[] = {7, 7, 14, 10, 12, 13, 25, 25, 13, 13};
   int b = 0;
   while (b < 9 && M > kBucket[b]) ++b;
@@ -725,7 +813,7 @@ Plan make_plan(int dtype, int epi, int M, int N, int K) {
   return make_plan_cfg(dtype, epi, M, N, K, pick_cfg(M, N, epi == kEpiSwiglu));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI, bool PF = false>
 hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hipStream_t s) {
   constexpr bool DUAL = EPI == kEpiSwiglu;
   if constexpr (DUAL && ((BN / WAVES_N / 16) % 2 != 0)) {
@@ -746,11 +834,11 @@ hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hi
         if (!attr) {
           (void)hipFuncSetAttribute(
               reinterpret_cast<const void*>(
-                  &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true>),
+                  &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true, PF>),
               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
           attr = true;
         }
-        gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true>
+        gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, true, PF>
             <<<grid, threads, lds, s>>>((const bf16_t*)a.A, (const bf16_t*)a.W,
                                         (const bf16_t*)a.W2, ep, a.K, p.k_per_split, p.tiles_m,
                                         p.tiles_n, partial);
@@ -765,11 +853,11 @@ hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hi
       if (!attr) {
         (void)hipFuncSetAttribute(
             reinterpret_cast<const void*>(
-                &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, false>),
+                &gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, false, PF>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         attr = true;
       }
-      gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, false>
+      gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI, false, PF>
           <<<grid, threads, lds, s>>>((const bf16_t*)a.A, (const bf16_t*)a.W,
                                       (const bf16_t*)a.W2, ep, a.K, p.k_per_split, p.tiles_m,
                                       p.tiles_n, nullptr);
@@ -816,7 +904,12 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
     case 31: return run_mfma<192, 128, 4, 1, 4, 64, EPI>(a, p, ep, ws, s);
     case 32: return run_mfma<128, 128, 4, 1, 2, 64, EPI>(a, p, ep, ws, s);
     case 33: return run_mfma<192, 192, 4, 2, 2, 64, EPI>(a, p, ep, ws, s);
-    default: return run_mfma<192, 192, 2, 2, 2, 64, EPI>(a, p, ep, ws, s);
+    case 34: return run_mfma<192, 192, 2, 2, 2, 64, EPI>(a, p, ep, ws, s);
+    case 35: return run_mfma<192, 192, 4, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 36: return run_mfma<192, 128, 2, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 37: return run_mfma<256, 128, 4, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 38: return run_mfma<128, 128, 2, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
+    default: return run_mfma<128, 256, 2, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
   }
 }
 
@@ -908,8 +1001,8 @@ int pick_qkv_cfg(int M) {
   if (M <= 128) return 1;   // 64x128
   if (M <= 192) return 6;   // 96x128
   if (M <= 256) return 8;   // 128x128, 8 waves
-  if (M <= 384) return 28;  // 192x128, 8 waves
-  return 9;                 // 256x128, 8 waves
+  if (M <= 384) return 36;  // 192x128, 8 waves, fragment prefetch
+  return 37;                // 256x128, 8 waves, fragment prefetch
 }
 
 hipError_t launch_gemm(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -943,7 +1036,17 @@ namespace {
 // 256 < M <= 384, else the plain LM-head choice.
 int pick_logits_stats_cfg(int M, int N) {
   if (M > 256 && M <= 384) return 12;
-  return pick_cfg(M, N, false);
+  const int c = pick_cfg(M, N, false);
+  // the statistics epilogue is not built for the fragment-prefetch tiles:
+  // their plain twins
+  switch (c) {
+    case 35: return 13;
+    case 36: return 28;
+    case 37: return 9;
+    case 38: return 8;
+    case 39: return 10;
+    default: return c;
+  }
 }
 
 Plan logits_stats_plan(int M, int N, int K, int cfg) {

@@ -523,8 +523,29 @@ def test_rope_scatter(bf16):
     assert (np.moveaxis(vcn, 3, 2)[np.broadcast_to(~touched[:, None, :], kcn.shape[:3])] == 3.0).all()
 
 
+@pytest.mark.parametrize("cfg", [35, 36, 37, 38, 39])
+@pytest.mark.parametrize("epi", [L.DLM_EPI_STORE_F32, L.DLM_EPI_SWIGLU])
+def test_gemm_prefetch_tiles_long_k(cfg, epi):
+    """The fragment-prefetch tiles over a long K (64 k-slices: the steady
+    two-step loop and every tail length), ragged M and N, against the oracle."""
+    for M, N, K in [(200, 300, 4096), (77, 130, 64 * 7), (5, 40, 64 * 5)]:
+        A, W, W2 = _gemm_inputs(M, N, K, seed=cfg + K)
+        g = oracle.unit_linear(A, W)
+        if epi == L.DLM_EPI_SWIGLU:
+            u = oracle.unit_linear(A, W2)
+            want = g / (1 + np.exp(-g)) * u
+            C = ops.gemm_config(epi, _dev(A), _dev(W), cfg, 1, W2=_dev(W2))
+            tol = 2.0 ** -8 * np.abs(want) + 1e-5
+        else:
+            want = g
+            C = ops.gemm_config(epi, _dev(A), _dev(W), cfg, 1)
+            tol = 2e-5 * max(1.0, np.abs(want).max())
+        got = _f64(C)
+        assert (np.abs(got - want) <= tol).all(), (M, N, K, np.abs(got - want).max())
+
+
 QKV_CFGS = [0, 1, 2, 4, 5, 6, 8, 9, 11, 12, 15, 16, 17, 18, 19, 21, 22, 23, 25, 28, 29, 30, 31,
-            32]  # every tile configuration with 128-column (one-head) tiles
+            32, 36, 37, 38]  # every tile configuration with 128-column (one-head) tiles
 
 
 def _qkv_fused_case(M, N, cfg, seed):
