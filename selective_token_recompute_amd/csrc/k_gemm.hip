@@ -332,41 +332,26 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
       read_frags(0, f0);
       wait_lgkm0();
     }
-    // steady step: slice kt+1 lands, slice kt+3 is issued (kt + 3 < KT)
+    // step kt: slice kt+1 lands (the last step re-reads slice kt, which no
+    // load overwrites any more, so that the reads and the MFMAs stay in one
+    // block), slice kt+3 is issued while kt + 3 < KT
     auto step = [&](int kt, Frags& cur, Frags& nxt) __attribute__((always_inline)) {
-      wait_slices<IPW, 3>(1);
+      wait_slices<IPW, 3>(min(1, max(0, KT - 2 - kt)));
       lds_barrier();
-      issue(kt + 3);
-      read_frags(kt + 1, nxt);
+      if (kt + 3 < KT) issue(kt + 3);
+      read_frags(min(kt + 1, KT - 1), nxt);
       mma(cur);
-      __builtin_amdgcn_sched_group_barrier(0x010, IPW, 0);
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, MT - RT * PER, 0);
-      wait_lgkm0();  // this wave's reads of slot kt+1 are done before the next barrier
+      wait_lgkm0();  // this wave's reads are done before the next barrier
     };
-    // last steps: nothing more to issue, no read after the last slice
-    auto tail = [&](int kt, Frags& cur, Frags& nxt) __attribute__((always_inline)) {
-      if (kt + 1 < KT) {
-        wait_slices<IPW, 3>(min(1, max(0, KT - 2 - kt)));
-        lds_barrier();
-        if (kt + 3 < KT) issue(kt + 3);
-        read_frags(kt + 1, nxt);
-      }
-      mma(cur);
-      wait_lgkm0();
-    };
-    int kt = 0;
-    for (; kt + 4 < KT; kt += 2) {
+    for (int kt = 0; kt < KT; kt += 2) {
       step(kt, f0, f1);
-      step(kt + 1, f1, f0);
-    }
-    for (; kt < KT; kt += 2) {
-      tail(kt, f0, f1);
-      if (kt + 1 < KT) tail(kt + 1, f1, f0);
+      if (kt + 1 < KT) step(kt + 1, f1, f0);
     }
   }
 
