@@ -154,6 +154,42 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     log(f"copy calibration: {reps} copies of {nbytes} bytes")
 
 
+def measured_ceilings():
+    """Ceilings measured on this GPU: a plain 1 GiB device-to-device copy
+    (read + write bytes over its event time) and this library's own bf16 GEMM
+    (default tile plan, plain fp32 store) on an 8192 x 8192 x 8192 problem."""
+    import torch
+    from selective_token_recompute_amd import ops, _lib as L
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def timed(f, reps):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    S = 8192
+    A = torch.randn(S, S, device="cuda").to(torch.bfloat16)
+    W = torch.randn(S, S, device="cuda").mul_(0.02).to(torch.bfloat16)
+    C = torch.empty(S, S, device="cuda")
+    t_gemm = timed(lambda: ops.gemm(L.DLM_EPI_STORE_F32, A, W, C=C), 10)
+    del A, W, C
+    torch.cuda.empty_cache()
+    return dict(hbm_copy_gbs=round(2 * 4 * n / t_copy / 1e9, 1),
+                gemm_bf16_tflops=round(2.0 * S ** 3 / t_gemm / 1e12, 1),
+                note="1 GiB device copy (read + write); this library's GEMM, 8192^3 bf16, "
+                     "default plan")
+
+
 def cpu_baseline(shape, run):
     """Oracle on a bounded sample: one full-width layer at step 0 (M = 512
     active rows, attention over N = 512) plus the LM head and statistics for
@@ -331,6 +367,8 @@ def main():
                     help="time whole runs of the extra configurations")
     ap.add_argument("--repeats", type=int, default=3,
                     help="extra timed regions of the configured setting (spread only)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured copy / GEMM ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 1 GiB device copies (counter calibration for profiles)")
     args = ap.parse_args()
@@ -368,6 +406,7 @@ def main():
     # the configured setting's timed region again, for its run-to-run spread
     spread = [K / nat_dt for nat_dt in (run_steps(factory("natural"), K)[0]
                                         for _ in range(args.repeats))]
+    regions = sorted([K / results["natural"]["seconds"]] + spread)
 
     # per-kernel event timing over the same steps (configured setting)
     _, _, ms_nat, tim = run_steps(factory("natural"), K, timing=True)
@@ -405,8 +444,10 @@ def main():
                    "global_batch": run.batch, "seq_len": run.seq_len, "parallelism": "none"},
         "mean_active_rows": round(sum(nat["ms"]) / len(nat["ms"]), 1),
         "repeats": dict(steps_per_s=[round(v, 3) for v in spread],
+                        median=round(regions[len(regions) // 2], 3), min=round(regions[0], 3),
+                        max=round(regions[-1], 3),
                         note="the same K timed steps run again after the timed region "
-                             "(not part of value)"),
+                             "(not part of value); median / min / max over all regions"),
         "roofline": roof,
         "kernels": kernels,
     }
@@ -418,6 +459,13 @@ def main():
     for name in [c for c in args.extra_configs.split(",") if c]:
         log(f"{name} ...")
         out[name] = extra_config(name, args.extra_steps, args.full_runs)
+    if not args.no_ceilings:
+        log("measured ceilings ...")
+        out["ceilings"] = measured_ceilings()
+        ach = out["roofline"]["achieved"]
+        ceil = out["ceilings"]["gemm_bf16_tflops" if out["roofline"]["bound"] == "mfma"
+                               else "hbm_copy_gbs"]
+        out["roofline"]["frac_of_measured_ceiling"] = round(ach / ceil, 4) if ceil else None
     if not args.no_layer_sweep:
         log("single-layer roofline sweep ...")
         out["layer_isolation"] = layer_isolation()
