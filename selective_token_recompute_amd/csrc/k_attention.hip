@@ -120,7 +120,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
-        const bf16x8 a = *(const bf16x8*)&sK[(kb * 16 + (lane & 15)) * KP + c * 32 + (lane >> 4) * 8];
+        const bf16x8 a =
+            *(const bf16x8*)&sK[(kb * 16 + (lane & 15)) * KP + c * 32 + (lane >> 4) * 8];
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[kb], 0, 0, 0);
       }
     }
@@ -216,19 +217,23 @@ __device__ __forceinline__ int vswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // instructions: permlane16_swap(v, v) returns v from lanes l and l^16 in its
 // two outputs, permlane32_swap(v, v) from lanes l and l^32.
 __device__ __forceinline__ float xor16_max(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto r =
+      __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto r =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor16_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto r =
+      __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ float xor32_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const auto r =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -449,7 +454,8 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
     const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
     const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - m);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) oacc[cb] = oacc[cb] * a0 + ((const f32x4*)mine)[cb * 64 + lane] * a1;
+    for (int cb = 0; cb < NCB; ++cb)
+      oacc[cb] = oacc[cb] * a0 + ((const f32x4*)mine)[cb * 64 + lane] * a1;
     l_run = l_run * a0 + ml.y * a1;
     m_run = m;
   }
@@ -636,13 +642,17 @@ void launch_attn_kernel(dim3 grid, bool dma, int stages, int kh, const void* q,
                         int kps, int M, float* po, float* pml, hipStream_t s) {
   if (dma) {
     if (stages == 2 && kh == 2)
-      launch_attn_dma<HD, SPLIT, 2, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
+      launch_attn_dma<HD, SPLIT, 2, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po,
+                                         pml, s);
     else if (stages == 2)
-      launch_attn_dma<HD, SPLIT, 2, 1>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
+      launch_attn_dma<HD, SPLIT, 2, 1>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po,
+                                         pml, s);
     else if (kh == 2)
-      launch_attn_dma<HD, SPLIT, 4, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
+      launch_attn_dma<HD, SPLIT, 4, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po,
+                                         pml, s);
     else
-      launch_attn_dma<HD, SPLIT, 4, 1>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po, pml, s);
+      launch_attn_dma<HD, SPLIT, 4, 1>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po,
+                                         pml, s);
   } else {
     attn_mfma_kernel<HD, SPLIT><<<grid, 256, 0, s>>>((const bf16_t*)q, row_start,
                                                      (const bf16_t*)kc, (const bf16_t*)vc,
@@ -659,16 +669,16 @@ hipError_t run_attn_mfma(const AttnPlan& p, int M, int B, int N, int nq, int nkv
   if (p.splits > 1) {
     float* po = (float*)ws;
     float* pml = po + (size_t)p.splits * M * nq * HD;
-    launch_attn_kernel<HD, true>(grid, dma, p.stages, p.key_halves, q, row_start, kc, vc, o, N, nq, nkv,
-                                 p.keys_per_split, M, po, pml, s);
+    launch_attn_kernel<HD, true>(grid, dma, p.stages, p.key_halves, q, row_start, kc, vc, o, N, nq,
+                                 nkv, p.keys_per_split, M, po, pml, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t total = (size_t)M * nq * (HD / 4);
     const int gsz = (int)std::min<size_t>((total + 255) / 256, 8192);
     attn_combine_kernel<bf16_t><<<gsz, 256, 0, s>>>(po, pml, p.splits, M * nq, HD, (bf16_t*)o);
   } else {
-    launch_attn_kernel<HD, false>(grid, dma, p.stages, p.key_halves, q, row_start, kc, vc, o, N, nq, nkv,
-                                  p.keys_per_split, M, nullptr, nullptr, s);
+    launch_attn_kernel<HD, false>(grid, dma, p.stages, p.key_halves, q, row_start, kc, vc, o, N, nq,
+                                  nkv, p.keys_per_split, M, nullptr, nullptr, s);
   }
   return hipGetLastError();
 }

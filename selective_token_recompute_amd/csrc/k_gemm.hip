@@ -5,18 +5,20 @@
 // projection and the FFN; only the active subset gets fresh Q/K/V; FFN cost
 // falls to O(M_t d^2) (§2 algorithmic complexity).  M shrinks from step to
 // step, so the launch plan depends on M: large M is MFMA-bound (bf16
-// 16x16x32 MFMA, LDS double buffering), small M is bound by streaming the
-// weights once (narrow row tile, split-K across workgroups, deterministic
-// two-pass reduction).
+// 16x16x32 MFMA fed from an LDS ring of k-slices, with fragment prefetch on
+// the 8-wave tiles), small M is bound by streaming the weights once (narrow
+// row tiles, split-K across workgroups whose partial sums are added in split
+// order, by a reduction kernel or by the next residual RMSNorm).
 //
-// Epilogues: plain float store (QKV, before the rotary step), residual add
-// into the float residual stream (out-projection, down-projection), SwiGLU
-// over a gate/up pair of weight matrices (silu(A Wg^T) * (A Wu^T), stored in
-// the storage type), and logits scattered to each row's (seq, pos) slot with
-// the mask token's column forced to -inf; the last optionally also folds
-// each row's logits, with the row's previous-step logits, into the partial
-// posterior statistics (log-normaliser, argmax, confidence, KL) of its column
-// tile, so that no separate pass re-reads the current logits.
+// Epilogues: plain float store, residual add into the float residual stream
+// (out-projection, down-projection), SwiGLU over a gate/up pair of weight
+// matrices (silu(A Wg^T) * (A Wu^T), stored in the storage type), QKV with
+// the rotary embedding and the K / V^T cache scatter, and logits scattered to
+// each row's (seq, pos) slot with the mask token's column forced to -inf; the
+// last optionally also folds each row's logits, with the row's previous-step
+// logits, into the partial posterior statistics (log-normaliser, argmax,
+// confidence, KL) of its column tile, so that no separate pass re-reads the
+// current logits.
 #include <utility>
 
 #include "common.h"
@@ -699,7 +701,7 @@ constexpr TileCfg kCfgs[] = {
     {192, 128, 2, 2, 2, 64},  // 12: two workgroups per CU
     {256, 256, 2, 4, 2, 64},  // 13: 8 waves, 128x64 per wave
     {64, 64, 2, 2, 4, 64},    // 14
-    {192, 128, 4, 1, 2, 64},  // 15: one head per wave (fused QKV epilogue)
+    {192, 128, 4, 1, 2, 64},  // 15: one head per wave
     {128, 128, 4, 1, 3, 64},  // 16: one head per wave
     {256, 128, 4, 1, 2, 64},  // 17: one head per wave
     {64, 128, 4, 1, 4, 64},   // 18: one head per wave
@@ -831,7 +833,8 @@ hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hi
         if (e != hipSuccess) return e;
         const size_t total = (size_t)a.M * a.N;
         const int g = (int)std::min<size_t>((total + 255) / 256, 8192);
-        if (!p.defer_reduce) splitk_reduce_kernel<EPI, bf16_t><<<g, 256, 0, s>>>(partial, p.splits, ep);
+        if (!p.defer_reduce)
+          splitk_reduce_kernel<EPI, bf16_t><<<g, 256, 0, s>>>(partial, p.splits, ep);
       }
     } else {
       static bool attr = false;
@@ -1035,7 +1038,8 @@ int pick_logits_stats_cfg(int M, int N) {
 }
 
 Plan logits_stats_plan(int M, int N, int K, int cfg) {
-  Plan p = make_plan_cfg(kBF16, kEpiLogitsStats, M, N, K, cfg >= 0 ? cfg : pick_logits_stats_cfg(M, N));
+  Plan p = make_plan_cfg(kBF16, kEpiLogitsStats, M, N, K,
+                         cfg >= 0 ? cfg : pick_logits_stats_cfg(M, N));
   p.splits = 1;  // the epilogue needs complete sums
   p.k_per_split = K;
   p.ws = 0;
