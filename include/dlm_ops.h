@@ -134,8 +134,8 @@ int dlm_op_attention_config(int32_t dtype, int32_t M, int32_t batch, int32_t seq
  * [M][nq 128] rotated, K cache bf16 [batch][nkv][seq_len][128] rotated and
  * the transposed V cache bf16 [batch][nkv][128][seq_len]; rope_table as
  * dlm_op_rope_table writes it (null: no rotation).  cfg: -1 for the default
- * tile plan, else a tile configuration with 128-column tiles (else
- * DLM_E_UNSUPPORTED). */
+ * tile plan, else a tile configuration whose tile stages at least one wave
+ * row of fp32 results in its LDS ring (else DLM_E_UNSUPPORTED). */
 int dlm_op_gemm_qkv(int32_t M, int32_t K, int32_t nq, int32_t nkv, int32_t seq_len,
                     const void* A, const void* W, const int32_t* row_seq, const int32_t* row_pos,
                     const float* rope_table, void* q, void* kcache, void* vcache, int32_t cfg,

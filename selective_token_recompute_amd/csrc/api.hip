@@ -444,7 +444,7 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out) {
     const double by = V * (double)d * es + M * (double)d * es + M * (double)V * 8.0;
     h->flops += fl;
     TRY(timed(h, DLM_K_GEMM_LM_HEAD, by, fl, [&] { return launch_gemm_logits_stats(g, -1, s); }));
-    const int nparts = gemm_logits_stats_parts(M, V, -1);
+    const int nparts = gemm_logits_stats_parts(M, V, d, -1);
     TRY(timed(h, DLM_K_VOCAB_STATS, M * (double)nparts * kVocabPartBytes, 0.0, [&] {
       return launch_vocab_merge_parts(M, nparts, N, r.kl_dir, row_seq, row_pos,
                                       h->at<float>(y.lse[prv]), h->at<int32_t>(y.has_prev),
@@ -804,7 +804,7 @@ int dlm_op_vocab_stats(int32_t M, int32_t V, int32_t mask_id, int32_t kl_dir, in
 size_t dlm_op_lm_head_stats_ws_bytes(int32_t M, int32_t V, int32_t K, int32_t cfg) {
   if (M < 0 || V < 2 || K < 1 || cfg >= gemm_num_configs()) return 0;
   if (!gemm_logits_stats_fusable(kBF16, K) || M == 0) return 0;
-  return (size_t)M * gemm_logits_stats_parts(M, V, cfg) * kVocabPartBytes;
+  return (size_t)M * gemm_logits_stats_parts(M, V, K, cfg) * kVocabPartBytes;
 }
 
 int dlm_op_lm_head_stats(int32_t M, int32_t V, int32_t K, const void* A, const void* W,
@@ -824,7 +824,7 @@ int dlm_op_lm_head_stats(int32_t M, int32_t V, int32_t K, const void* A, const v
     return DLM_E_INVALID;
   auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   if (!al16(A) || !al16(W)) return DLM_E_INVALID;
-  const int nparts = gemm_logits_stats_parts(M, V, cfg);
+  const int nparts = gemm_logits_stats_parts(M, V, K, cfg);
   if ((size_t)M * nparts * kVocabPartBytes > ws_bytes) return DLM_E_SIZE;
   hipStream_t s = (hipStream_t)stream;
   GemmArgs g{kBF16, kEpiLogitsStats, M, V, K, A, W, nullptr, z_cur, row_seq, row_pos, seq_len,

@@ -92,7 +92,7 @@ bool gemm_logits_stats_fusable(int dtype, int K);
 // Whether the fused form is the faster one at this M (else the LM head with
 // kEpiLogits followed by launch_vocab_stats).
 bool gemm_logits_stats_preferred(int M, int N);
-int gemm_logits_stats_parts(int M, int N, int cfg);
+int gemm_logits_stats_parts(int M, int N, int K, int cfg);
 size_t gemm_logits_stats_bytes(int dtype, int M, int N, int K);
 hipError_t launch_gemm_logits_stats(const GemmArgs& a, int cfg, hipStream_t s);
 

@@ -144,6 +144,15 @@ constexpr int qkv_wave_rows_per_pass(int waves_m, int wm, int row_bytes, int rin
   return 0;
 }
 
+// QKV column order inside each 128-wide head: the tile's column v holds the
+// weight row (output feature) with bits 5 and 6 of v swapped, an involution
+// that puts the rotary partners j and j + 64 of a half-split head into the
+// same 64-column chunk (chunk hb of a head holds j = 32 hb + w and
+// j + 64, w < 32), so a QKV tile may be any multiple of 64 columns wide.
+__host__ __device__ constexpr int qkv_col_swap(int v) {
+  return (v & ~0x60) | ((v & 0x20) << 1) | ((v & 0x40) >> 1);
+}
+
 template <bool B, typename T>
 __device__ __forceinline__ T& pick(T& a, T& b) {
   if constexpr (B) return b;
@@ -223,6 +232,7 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
         wb = up ? W2 : W;
       } else {
         grow = n0 + br;
+        if constexpr (EPI == kEpiQKV) grow = qkv_col_swap(grow);
         wb = W;
       }
       base = wb + (size_t)min(grow, N - 1) * K;
@@ -360,16 +370,20 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
   // epilogue
   const int rq = (lane >> 4) * 4, cl = lane & 15;
   if constexpr (EPI == kEpiQKV) {
-    // The tile is one head (BN = hd = 128).  The fp32 tile is staged in LDS
-    // (the operand ring is free by now), with each row's (sequence,
-    // position), in passes of whole wave rows when it does not fit at once,
-    // so that any thread can pair column c with c + 64 for the rotary
-    // embedding and the stores coalesce: q and K rows as packed bf16 pairs
-    // along the head dimension, V transposed with 4 consecutive positions per
-    // 8-byte store.  The item loops have compile-time trip counts and are
-    // unrolled so that their loads are all in flight together.
-    static_assert(BN == 128, "the fused QKV epilogue needs one head per tile");
-    constexpr int LDW = 132;  // padded LDS row stride (floats)
+    // The tile is BN/64 chunks of 64 columns in the swapped order of
+    // qkv_col_swap: chunk g of the q | k | v list is half hb = g & 1 of head
+    // g >> 1, with columns w < 32 holding head dimension 32 hb + w and
+    // columns 32 + w holding its rotary partner 64 + 32 hb + w.  The fp32
+    // tile is staged in LDS (the operand ring is free by now), with each
+    // row's (sequence, position), in passes of whole wave rows when it does
+    // not fit at once, so that any thread can pair a column with its partner
+    // for the rotary embedding and the stores coalesce: q and K rows as
+    // packed bf16 pairs along the head dimension, V transposed with 4
+    // consecutive positions per 8-byte store.  The item loops have
+    // compile-time trip counts and are unrolled so that their loads are all
+    // in flight together.
+    static_assert(BN % 64 == 0, "the fused QKV epilogue works on 64-column chunks");
+    constexpr int LDW = BN + 4;  // padded LDS row stride (floats)
     constexpr int NT = 64 * NW;
     constexpr int WMP = qkv_wave_rows_per_pass(WAVES_M, WM, LDW * 4 + 8, STAGES * STAGE_BYTES);
     static_assert(WMP >= 1, "one wave row of the tile must fit the LDS ring");
@@ -377,8 +391,8 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
     static_assert(PR % 4 == 0, "row quads");
     float* T = (float*)smem;
     int2* meta = (int2*)(smem + (size_t)PR * LDW * 4);  // (sequence, position) per row
-    const int hix = n0 / 128;  // head in the q | k | v list
     const int nq = ep.nq, nkv = ep.nkv, Nseq = ep.seq_len;
+    const int nheads = nq + 2 * nkv;
     auto pass = [&](auto P) __attribute__((always_inline)) {
       constexpr int p = decltype(P)::value;
       const int r0 = m0 + p * PR;  // first row of this pass
@@ -398,59 +412,72 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
         meta[r] = make_int2(ep.row_seq[rr], ep.row_pos[rr]);
       }
       __syncthreads();
-      if (hix < nq + nkv) {
-        // q or K head: item = (row, two consecutive rotary pairs jp, jp + 1)
-        constexpr int ITEMS = PR * 32, ITER = (ITEMS + NT - 1) / NT;
 #pragma unroll
-        for (int k = 0; k < ITER; ++k) {
-          const int it = tid + k * NT;
-          const int r = it >> 5, jp = (it & 31) * 2;
-          const int row = r0 + r;
-          if (it < ITEMS && row < M) {
-            const int2 sp = meta[r];
-            const float2 lo = *(const float2*)(T + r * LDW + jp);
-            const float2 hi = *(const float2*)(T + r * LDW + 64 + jp);
-            const float4 cs = ep.rope ? *(const float4*)(ep.rope + ((size_t)sp.y * 64 + jp) * 2)
-                                      : make_float4(1.f, 0.f, 1.f, 0.f);
-            bf16_t* dst = hix < nq ? ep.q + (size_t)row * nq * 128 + (size_t)hix * 128
-                                   : ep.kc + (((size_t)sp.x * nkv + (hix - nq)) * Nseq + sp.y) *
-                                                 128;
-            *(uint32_t*)(dst + jp) = f2bf2(lo.x * cs.x - hi.x * cs.y, lo.y * cs.z - hi.y * cs.w);
-            *(uint32_t*)(dst + 64 + jp) =
-                f2bf2(lo.x * cs.y + hi.x * cs.x, lo.y * cs.w + hi.y * cs.z);
-          }
-        }
-      } else {
-        // V head, stored transposed: item = (row quad, column c)
-        const int g = hix - nq - nkv;
-        constexpr int ITEMS = (PR / 4) * 128, ITER = (ITEMS + NT - 1) / NT;
+      for (int ch = 0; ch < BN / 64; ++ch) {
+        const int g = n0 / 64 + ch;
+        const int hix = g >> 1, hb = g & 1;  // head in the q | k | v list, its half
+        const float* Tc = T + ch * 64;
+        if (hix >= nheads) {
+          // columns past N: nothing to store
+        } else if (hix < nq + nkv) {
+          // q or K head: item = (row, two consecutive rotary pairs w, w + 1)
+          constexpr int ITEMS = PR * 16, ITER = (ITEMS + NT - 1) / NT;
 #pragma unroll
-        for (int k = 0; k < ITER; ++k) {
-          const int it = tid + k * NT;
-          const int c = it & 127, r4 = (it >> 7) * 4;
-          const int row = r0 + r4;
-          if (it < ITEMS && row < M) {
-            int2 sp[4];
-            float v[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              sp[t] = meta[r4 + t];
-              v[t] = T[(r4 + t) * LDW + c];
+          for (int k = 0; k < ITER; ++k) {
+            const int it = tid + k * NT;
+            const int r = it >> 4, w = (it & 15) * 2;
+            const int row = r0 + r;
+            if (it < ITEMS && row < M) {
+              const int2 sp = meta[r];
+              const int jp = hb * 32 + w;  // head dimension of the first pair
+              const float2 lo = *(const float2*)(Tc + r * LDW + w);
+              const float2 hi = *(const float2*)(Tc + r * LDW + 32 + w);
+              const float4 cs = ep.rope
+                                    ? *(const float4*)(ep.rope + ((size_t)sp.y * 64 + jp) * 2)
+                                    : make_float4(1.f, 0.f, 1.f, 0.f);
+              bf16_t* dst = hix < nq ? ep.q + (size_t)row * nq * 128 + (size_t)hix * 128
+                                     : ep.kc + (((size_t)sp.x * nkv + (hix - nq)) * Nseq + sp.y) *
+                                                   128;
+              *(uint32_t*)(dst + jp) =
+                  f2bf2(lo.x * cs.x - hi.x * cs.y, lo.y * cs.z - hi.y * cs.w);
+              *(uint32_t*)(dst + 64 + jp) =
+                  f2bf2(lo.x * cs.y + hi.x * cs.x, lo.y * cs.w + hi.y * cs.z);
             }
-            const bool packed = row + 3 < M && (Nseq & 3) == 0 && (sp[0].y & 3) == 0 &&
-                                sp[3].x == sp[0].x && sp[3].y == sp[0].y + 3 &&
-                                sp[1].x == sp[0].x && sp[1].y == sp[0].y + 1 &&
-                                sp[2].x == sp[0].x && sp[2].y == sp[0].y + 2;
-            if (packed) {
-              uint2 w;
-              w.x = f2bf2(v[0], v[1]);
-              w.y = f2bf2(v[2], v[3]);
-              *(uint2*)(ep.vc + (((size_t)sp[0].x * nkv + g) * 128 + c) * Nseq + sp[0].y) = w;
-            } else {
+          }
+        } else {
+          // V head, stored transposed: item = (row quad, chunk column w)
+          const int gv = hix - nq - nkv;
+          constexpr int ITEMS = (PR / 4) * 64, ITER = (ITEMS + NT - 1) / NT;
 #pragma unroll
-              for (int t = 0; t < 4; ++t)
-                if (row + t < M)
-                  ep.vc[(((size_t)sp[t].x * nkv + g) * 128 + c) * Nseq + sp[t].y] = f2bf(v[t]);
+          for (int k = 0; k < ITER; ++k) {
+            const int it = tid + k * NT;
+            const int w = it & 63, r4 = (it >> 6) * 4;
+            const int c = (w & 32) * 2 + hb * 32 + (w & 31);  // head dimension
+            const int row = r0 + r4;
+            if (it < ITEMS && row < M) {
+              int2 sp[4];
+              float v[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                sp[t] = meta[r4 + t];
+                v[t] = Tc[(r4 + t) * LDW + w];
+              }
+              const bool packed = row + 3 < M && (Nseq & 3) == 0 && (sp[0].y & 3) == 0 &&
+                                  sp[3].x == sp[0].x && sp[3].y == sp[0].y + 3 &&
+                                  sp[1].x == sp[0].x && sp[1].y == sp[0].y + 1 &&
+                                  sp[2].x == sp[0].x && sp[2].y == sp[0].y + 2;
+              if (packed) {
+                uint2 u;
+                u.x = f2bf2(v[0], v[1]);
+                u.y = f2bf2(v[2], v[3]);
+                *(uint2*)(ep.vc + (((size_t)sp[0].x * nkv + gv) * 128 + c) * Nseq + sp[0].y) = u;
+              } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  if (row + t < M)
+                    ep.vc[(((size_t)sp[t].x * nkv + gv) * 128 + c) * Nseq + sp[t].y] =
+                        f2bf(v[t]);
+              }
             }
           }
         }
@@ -726,6 +753,11 @@ constexpr TileCfg kCfgs[] = {
     {256, 128, 4, 2, 3, 64, true},  // 37: 9 with fragment prefetch
     {128, 128, 2, 4, 3, 64, true},  // 38: 8 with fragment prefetch
     {128, 256, 2, 4, 3, 64, true},  // 39: 10 with fragment prefetch
+    {96, 192, 2, 2, 3, 64, true},   // 40: 48x96 per wave, fragment prefetch
+    {64, 192, 2, 2, 3, 64, true},   // 41: 32x96 per wave, fragment prefetch
+    {128, 192, 2, 4, 3, 64, true},  // 42: 8 waves, 64x48 per wave, fragment prefetch
+    {128, 192, 4, 2, 3, 64, true},  // 43: 8 waves, 32x96 per wave, fragment prefetch
+    {96, 192, 2, 2, 3, 64},         // 44: 40 without fragment prefetch
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr bool cfgs_fit_lds() {
@@ -755,16 +787,17 @@ struct Plan {
 // 512, 8-wave tiles with fragment prefetch that give every CU one workgroup
 // (gate/up 192x192 at M = 384: 2 x 128 tiles); large M favours 256x256
 // tiles with 8 waves.
-int pick_cfg(int M, int N, bool dual) {
+int pick_cfg(int M, int N, int K, bool dual) {
   static const int kBucket[] = {16, 32, 64, 128, 192, 256, 320, 384, 512};
   static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 36, 36, 8, 13};
+  static const int kNarrowDeep[] = {7, 7, 1, 1, 6, 8, 36, 36, 37, 13};  // K >= 8192
   static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 37, 13};
   static const int kDual[] = {1, 1, 1, 8, 5, 37, 35, 35, 13, 13};
   static const int kWide[] = {7, 7, 14, 10, 12, 13, 25, 25, 13, 13};
   int b = 0;
   while (b < 9 && M > kBucket[b]) ++b;
   if (dual) return kDual[b];
-  if (N <= 8192) return kNarrow[b];
+  if (N <= 8192) return K >= 8192 ? kNarrowDeep[b] : kNarrow[b];
   if (N <= 32768) return kMedium[b];
   return kWide[b];
 }
@@ -797,7 +830,7 @@ Plan make_plan_cfg(int dtype, int epi, int M, int N, int K, int cfg) {
 }
 
 Plan make_plan(int dtype, int epi, int M, int N, int K) {
-  return make_plan_cfg(dtype, epi, M, N, K, pick_cfg(M, N, epi == kEpiSwiglu));
+  return make_plan_cfg(dtype, epi, M, N, K, pick_cfg(M, N, K, epi == kEpiSwiglu));
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI, bool PF = false>
@@ -805,8 +838,13 @@ hipError_t run_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* ws, hi
   constexpr bool DUAL = EPI == kEpiSwiglu;
   if constexpr (DUAL && ((BN / WAVES_N / 16) % 2 != 0)) {
     return hipErrorInvalidValue;  // a dual tile needs matching gate/up column tiles per wave
-  } else if constexpr (EPI == kEpiQKV && BN != 128) {
-    return hipErrorInvalidValue;  // the fused QKV epilogue needs one head per tile
+  } else if constexpr (EPI == kEpiQKV &&
+                       (BN % 64 != 0 ||
+                        qkv_wave_rows_per_pass(WAVES_M, BM / WAVES_M, (BN + 4) * 4 + 8,
+                                               STAGES * (BM + BN) * BK * 2) == 0)) {
+    // the fused QKV epilogue works on 64-column chunks and stages at least
+    // one wave row of the tile in the LDS ring
+    return hipErrorInvalidValue;
   } else {
     dim3 grid(p.tiles_m * p.tiles_n, p.splits, 1);
     const int threads = 64 * WAVES_M * WAVES_N;
@@ -897,7 +935,12 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
     case 36: return run_mfma<192, 128, 2, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 37: return run_mfma<256, 128, 4, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 38: return run_mfma<128, 128, 2, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
-    default: return run_mfma<128, 256, 2, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 39: return run_mfma<128, 256, 2, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 40: return run_mfma<96, 192, 2, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 41: return run_mfma<64, 192, 2, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 42: return run_mfma<128, 192, 2, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 43: return run_mfma<128, 192, 4, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
+    default: return run_mfma<96, 192, 2, 2, 3, 64, EPI>(a, p, ep, ws, s);
   }
 }
 
@@ -981,16 +1024,19 @@ bool gemm_qkv_fusable(int dtype, int M, int hd, int K) {
   return dtype == kBF16 && hd == 128 && K % kBK == 0 && M >= 1;
 }
 
-// Tile for the fused QKV epilogue by M, from a sweep of every 128-column
-// configuration at the LLaDA-8B shape (d 4096 -> 12288); at every M it beat
-// the plain GEMM followed by the separate rotary / scatter kernels.
+// Tile for the fused QKV epilogue by M, from a sweep of the configurations
+// at the LLaDA-8B shape (d 4096 -> 12288); at every M it beat the plain GEMM
+// followed by the separate rotary / scatter kernels.  The 192-column tiles
+// give 4 x 64 = 256 workgroups at M = 384 and 512 where 128-column tiles give
+// 192, but run each tile less efficiently (4 waves, or 48-column wave tiles),
+// so they gain only 2-9%.
 int pick_qkv_cfg(int M) {
   if (M <= 64) return 0;    // 32x128, 4 waves: weight streaming
   if (M <= 128) return 1;   // 64x128
   if (M <= 192) return 6;   // 96x128
   if (M <= 256) return 8;   // 128x128, 8 waves
-  if (M <= 384) return 36;  // 192x128, 8 waves, fragment prefetch
-  return 37;                // 256x128, 8 waves, fragment prefetch
+  if (M <= 384) return 44;  // 96x192, 4 waves
+  return 42;                // 128x192, 8 waves, fragment prefetch
 }
 
 hipError_t launch_gemm(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -1022,9 +1068,9 @@ namespace {
 // Tile of the fused LM head by M: the 4-wave 192x128 tile (two workgroups per
 // CU, so one workgroup's epilogue overlaps the other's main loop) for
 // 256 < M <= 384, else the plain LM-head choice.
-int pick_logits_stats_cfg(int M, int N) {
+int pick_logits_stats_cfg(int M, int N, int K) {
   if (M > 256 && M <= 384) return 12;
-  const int c = pick_cfg(M, N, false);
+  const int c = pick_cfg(M, N, K, false);
   // the statistics epilogue is not built for the fragment-prefetch tiles:
   // their plain twins
   switch (c) {
@@ -1039,7 +1085,7 @@ int pick_logits_stats_cfg(int M, int N) {
 
 Plan logits_stats_plan(int M, int N, int K, int cfg) {
   Plan p = make_plan_cfg(kBF16, kEpiLogitsStats, M, N, K,
-                         cfg >= 0 ? cfg : pick_logits_stats_cfg(M, N));
+                         cfg >= 0 ? cfg : pick_logits_stats_cfg(M, N, K));
   p.splits = 1;  // the epilogue needs complete sums
   p.k_per_split = K;
   p.ws = 0;
@@ -1057,14 +1103,14 @@ bool gemm_logits_stats_preferred(int M, int N) {
   return M <= 64 || (M > 256 && M <= 384);
 }
 
-int gemm_logits_stats_parts(int M, int N, int cfg) {
+int gemm_logits_stats_parts(int M, int N, int K, int cfg) {
   if (M <= 0 || (cfg >= kNumCfgs)) return 0;
-  return logits_stats_plan(M, N, kBK, cfg).tiles_n;
+  return logits_stats_plan(M, N, K, cfg).tiles_n;
 }
 
 size_t gemm_logits_stats_bytes(int dtype, int M, int N, int K) {
   if (!gemm_logits_stats_fusable(dtype, K) || M <= 0) return 0;
-  return (size_t)M * gemm_logits_stats_parts(M, N, -1) * sizeof(VocabPart);
+  return (size_t)M * gemm_logits_stats_parts(M, N, K, -1) * sizeof(VocabPart);
 }
 
 hipError_t launch_gemm_logits_stats(const GemmArgs& a, int cfg, hipStream_t s) {
