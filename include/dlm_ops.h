@@ -112,18 +112,20 @@ int dlm_op_attention(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, i
                      size_t ws_bytes, void* stream);
 /* The same attention with a forced split of the keys (splits > 0: that many
  * key ranges, partial results merged by log-sum-exp in a second pass; 0:
- * the default plan), LDS ring depth (stages 2 or 4; 0: the plan's) and
- * number of waves sharing each block of 16 queries (key_halves 1 or 2, each
- * wave over its share of every key tile, merged by log-sum-exp; 0: the
- * plan's), for tuning sweeps.  ws must hold
- * dlm_op_attention_config_ws_bytes() bytes; DLM_E_SIZE otherwise. */
+ * the default plan), LDS ring depth (stages 2 or 4; 0: the plan's), number
+ * of key groups (key_halves 1, 2 or 4: waves sharing each block of 16
+ * queries, each over its share of every key tile, merged by log-sum-exp; 0:
+ * the plan's) and 16-query blocks per wave (qblocks 1 or 2; 0: the plan's),
+ * for tuning sweeps; the layouts built are (key groups, query blocks) =
+ * (1, 1), (2, 1), (4, 1), (2, 2), (4, 2), any other pair runs (2, 1).  ws
+ * must hold dlm_op_attention_config_ws_bytes() bytes; DLM_E_SIZE otherwise. */
 size_t dlm_op_attention_config_ws_bytes(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len,
                                         int32_t nq, int32_t nkv, int32_t hd, int32_t splits);
 int dlm_op_attention_config(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, int32_t nq,
                             int32_t nkv, int32_t hd, const void* q, const int32_t* row_start,
                             const void* kcache, const void* vcache, void* o, int32_t splits,
-                            int32_t stages, int32_t key_halves, void* ws, size_t ws_bytes,
-                            void* stream);
+                            int32_t stages, int32_t key_halves, int32_t qblocks, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* QKV projection with the rotary embedding and the K/V cache scatter in the
  * GEMM epilogue (SureLock page, §2: fresh Q/K/V only for the active rows,

@@ -261,17 +261,29 @@ __device__ __forceinline__ void attn_lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int HD, bool SPLIT, int STAGES, int KH>
-__global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
+// Wave layout: QW = 4 / QB query waves of 16 QB queries each, times KH key
+// groups.  Wave (kh, qw) takes keys [kh * 64 / KH, (kh + 1) * 64 / KH) of
+// every 64-key tile with its own online-softmax state per 16-query block; the
+// KH states of a query block are merged through LDS at the end, in pairs.
+// With QB = 2 every K and V^T fragment read from LDS feeds the MFMAs of two
+// query blocks, which halves the LDS reads per query (the loop over key tiles
+// is bound by LDS bandwidth and latency, not by HBM).
+template <int HD, int KH, int QB>
+constexpr size_t attn_merge_bytes() {
+  return KH == 1 ? 0
+                 : (size_t)(KH / 2) * (4 / QB) * (QB * (HD / 16) * 64 * 16 + QB * 64 * 8);
+}
+
+template <int HD, bool SPLIT, int STAGES, int KH, int QB>
+__global__ __launch_bounds__(64 * (4 / QB) * KH) void attn_mfma_dma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ row_start,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ o, int N,
     int nq, int nkv, int keys_per_split, int M, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-  // KH waves share each block of 16 queries: wave (kh, qw) takes keys
-  // [kh * 64 / KH, (kh + 1) * 64 / KH) of every 64-key tile with its own
-  // online-softmax state; the KH states are merged through LDS at the end.
-  static_assert(KH == 1 || KH == 2, "key halves");
-  constexpr int NWV = 4 * KH;                       // waves
+  static_assert(KH == 1 || KH == 2 || KH == 4, "key groups");
+  static_assert(QB == 1 || QB == 2, "query blocks per wave");
+  constexpr int QW = 4 / QB;                        // query waves
+  constexpr int NWV = QW * KH;                      // waves
   constexpr int NKB = 4 / KH;                       // 16-key blocks per wave per tile
   constexpr int NKC = HD / 32, NCB = HD / 16;
   constexpr int KCH = HD / 8;                       // 16-byte chunks per K row
@@ -280,10 +292,11 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
   constexpr int K_INSTR = K_BYTES / 1024, V_INSTR = V_BYTES / 1024;
   constexpr int IPW = (K_INSTR + V_INSTR) / NWV;    // per wave
   static_assert((K_INSTR + V_INSTR) % NWV == 0, "instructions per wave");
+  static_assert((STAGES - 1) * IPW < 64, "in-flight loads must fit the vmcnt counter");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qw = wave & 3, kh = wave >> 2;
+  const int qw = wave % QW, kh = wave / QW;
   // XCD-aware order: workgroup i (x fastest) runs on XCD i % 8; give
   // consecutive workgroups of one XCD the query tiles of one (sequence,
   // kv head), which then read its K/V slab through that XCD's L2.
@@ -300,11 +313,16 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
   const int qbase = bx * kAttnQ;
   if (qbase >= Qn) return;  // uniform over the workgroup
 
-  const int qv = qbase + qw * 16 + (lane & 15);
-  const bool qok = qv < Qn;
-  const bool wave_live = qbase + qw * 16 < Qn;  // wave-uniform
-  const int row = r0 + (qok ? qv / G : 0);
-  const int head = g * G + (qok ? qv % G : 0);
+  bool qok[QB];
+  int row[QB], head[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qv = qbase + (qw * QB + qb) * 16 + (lane & 15);
+    qok[qb] = qv < Qn;
+    row[qb] = r0 + (qok[qb] ? qv / G : 0);
+    head[qb] = g * G + (qok[qb] ? qv % G : 0);
+  }
+  const bool wave_live = qbase + qw * QB * 16 < Qn;  // wave-uniform
   const size_t slab = ((size_t)b * nkv + g) * N * HD;
   const bf16_t* kslab = kc + slab;  // [N][HD]
   const bf16_t* vslab = vc + slab;  // [HD][N]
@@ -342,25 +360,32 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 oacc[NCB];
+  float m_run[QB], l_run[QB];
+  f32x4 oacc[QB][NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) oacc[qb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
     if (t < ntiles) issue(t);
   // the query fragments load while the first tiles are in flight
-  bf16x8 qf[NKC];
-  {
-    const bf16_t* qp = q + (size_t)row * nq * HD + (size_t)head * HD + (lane >> 4) * 8;
+  bf16x8 qf[QB][NKC];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bf16_t* qp =
+        q + (size_t)row[qb] * nq * HD + (size_t)head[qb] * HD + (lane >> 4) * 8;
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
-      if (qok) {
-        qf[c] = *(const bf16x8*)(qp + c * 32);
+      if (qok[qb]) {
+        qf[qb][c] = *(const bf16x8*)(qp + c * 32);
       } else {
         const uint4 z = make_uint4(0, 0, 0, 0);
-        qf[c] = *(const bf16x8*)&z;
+        qf[qb][c] = *(const bf16x8*)&z;
       }
     }
   }
@@ -374,17 +399,20 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
     if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1);
     if (!wave_live) continue;  // no query of this wave is valid: loads only
     const unsigned char* st = smem + (t % STAGES) * STAGE;
-    f32x4 s[NKB];
+    f32x4 s[QB][NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int r = kofs + kb * 16 + (lane & 15);
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
         const int lc = c * 4 + (lane >> 4);
         const bf16x8 a =
             *(const bf16x8*)(st + r * (HD * 2) + ((lc ^ kswz(r, KCH)) << 4));
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], s[kb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][c], s[qb][kb], 0, 0, 0);
       }
     }
     // Online softmax in base 2 on the scaled scores.  The running maximum of
@@ -392,37 +420,40 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
     // maximum exceeds it by more than kLazyMax; otherwise the exponentials
     // are taken against the stale maximum and stay below 2^kLazyMax.  The
     // normalised result is the same either way.
-    float mx = -INFINITY;
+    s16x4 pb[QB][NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = xor16_max(mx);
-    mx = xor32_max(mx);
-    mx *= scale;
-    if (__any(mx > m_run + kLazyMax)) {  // wave-uniform branch
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // m_run = -inf -> 0
-      l_run *= alpha;
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) oacc[cb] *= alpha;
-      m_run = m_new;
-    }
-    float psum = 0.f;
-    s16x4 pb[NKB];
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+      mx = xor16_max(mx);
+      mx = xor32_max(mx);
+      mx *= scale;
+      if (__any(mx > m_run[qb] + kLazyMax)) {  // wave-uniform branch
+        const float m_new = fmaxf(m_run[qb], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);  // -inf -> 0
+        l_run[qb] *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], scale, -m_run));
-        psum += p[i];
+        for (int cb = 0; cb < NCB; ++cb) oacc[qb][cb] *= alpha;
+        m_run[qb] = m_new;
       }
-      const u32x2 w = {f2bf2(p[0], p[1]), f2bf2(p[2], p[3])};
-      pb[kb] = __builtin_bit_cast(s16x4, w);
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], scale, -m_run[qb]));
+          psum += p[i];
+        }
+        const u32x2 w = {f2bf2(p[0], p[1]), f2bf2(p[2], p[3])};
+        pb[qb][kb] = __builtin_bit_cast(s16x4, w);
+      }
+      psum = xor32_sum(xor16_sum(psum));
+      l_run[qb] += psum;
     }
-    psum = xor32_sum(xor16_sum(psum));
-    l_run += psum;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int vr = cb * 16 + (lane & 15);
@@ -431,58 +462,82 @@ __global__ __launch_bounds__(256 * KH) void attn_mfma_dma_kernel(
         const int u = (kofs + kb * 16) / 4 + (lane >> 4);  // 8-byte unit: 4 keys
         const s16x4 va = *(const s16x4*)(st + K_BYTES + vr * 128 +
                                           (((u >> 1) ^ vswz(vr)) << 4) + ((u & 1) << 3));
-        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kb], oacc[cb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][cb] =
+              __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[qb][kb], oacc[qb][cb], 0, 0, 0);
       }
     }
   }
 
-  if constexpr (KH == 2) {
-    // merge the second key half into the first: (m, l, o) of two disjoint
-    // key sets combine by the log-sum-exp rule
+  if constexpr (KH > 1) {
+    // merge the key groups in pairs, (m, l, o) of disjoint key sets by the
+    // log-sum-exp rule: in the round of width h the groups [h, 2h) hand
+    // their state to the groups [0, h) through LDS; every wave takes part in
+    // every barrier
+    constexpr int REG = QB * NCB * 64 * 16 + QB * 64 * 8;  // o fragments + (m, l)
     attn_lds_barrier();  // every wave is done with the tiles in LDS
-    constexpr int REG = NCB * 64 * 16 + 64 * 8;  // o fragments + (m, l) per lane
-    unsigned char* mine = smem + qw * REG;
-    if (kh == 1) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) ((f32x4*)mine)[cb * 64 + lane] = oacc[cb];
-      ((float2*)(mine + NCB * 64 * 16))[lane] = make_float2(m_run, l_run);
+    for (int h = KH / 2; h >= 1; h /= 2) {
+      if (kh >= h && kh < 2 * h) {
+        unsigned char* mine = smem + ((kh - h) * QW + qw) * REG;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            ((f32x4*)mine)[(qb * NCB + cb) * 64 + lane] = oacc[qb][cb];
+          ((float2*)(mine + QB * NCB * 64 * 16))[qb * 64 + lane] =
+              make_float2(m_run[qb], l_run[qb]);
+        }
+      }
+      attn_lds_barrier();
+      if (kh < h) {
+        const unsigned char* other = smem + (kh * QW + qw) * REG;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float2 ml = ((const float2*)(other + QB * NCB * 64 * 16))[qb * 64 + lane];
+          const float m = fmaxf(m_run[qb], ml.x);
+          const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m);
+          const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - m);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            oacc[qb][cb] =
+                oacc[qb][cb] * a0 + ((const f32x4*)other)[(qb * NCB + cb) * 64 + lane] * a1;
+          l_run[qb] = l_run[qb] * a0 + ml.y * a1;
+          m_run[qb] = m;
+        }
+      }
+      attn_lds_barrier();  // the slots are read before the next round writes
     }
-    attn_lds_barrier();
-    if (kh == 1) return;
-    const float2 ml = ((const float2*)(mine + NCB * 64 * 16))[lane];
-    const float m = fmaxf(m_run, ml.x);
-    const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-    const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - m);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      oacc[cb] = oacc[cb] * a0 + ((const f32x4*)mine)[cb * 64 + lane] * a1;
-    l_run = l_run * a0 + ml.y * a1;
-    m_run = m;
+    if (kh != 0) return;
   }
 
-  if (!qok) return;
-  const int gq = row * nq + head;
-  if (SPLIT) {
-    const size_t base = (size_t)bz * M * nq + gq;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      *(f32x4*)(part_o + base * HD + cb * 16 + (lane >> 4) * 4) = oacc[cb];
-    if ((lane >> 4) == 0) {
-      part_ml[base * 2] = m_run;
-      part_ml[base * 2 + 1] = l_run;
-    }
-  } else {
-    const float inv = 1.f / l_run;
-    bf16_t* op = o + (size_t)row * nq * HD + (size_t)head * HD;
+  for (int qb = 0; qb < QB; ++qb) {
+    if (!qok[qb]) continue;
+    const int gq = row[qb] * nq + head[qb];
+    if (SPLIT) {
+      const size_t base = (size_t)bz * M * nq + gq;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int c = cb * 16 + (lane >> 4) * 4;
-      ushort4 w;
-      w.x = f2bf(oacc[cb][0] * inv);
-      w.y = f2bf(oacc[cb][1] * inv);
-      w.z = f2bf(oacc[cb][2] * inv);
-      w.w = f2bf(oacc[cb][3] * inv);
-      *(ushort4*)(op + c) = w;
+      for (int cb = 0; cb < NCB; ++cb)
+        *(f32x4*)(part_o + base * HD + cb * 16 + (lane >> 4) * 4) = oacc[qb][cb];
+      if ((lane >> 4) == 0) {
+        part_ml[base * 2] = m_run[qb];
+        part_ml[base * 2 + 1] = l_run[qb];
+      }
+    } else {
+      const float inv = 1.f / l_run[qb];
+      bf16_t* op = o + (size_t)row[qb] * nq * HD + (size_t)head[qb] * HD;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int c = cb * 16 + (lane >> 4) * 4;
+        ushort4 w;
+        w.x = f2bf(oacc[qb][cb][0] * inv);
+        w.y = f2bf(oacc[qb][cb][1] * inv);
+        w.z = f2bf(oacc[qb][cb][2] * inv);
+        w.w = f2bf(oacc[qb][cb][3] * inv);
+        *(ushort4*)(op + c) = w;
+      }
     }
   }
 }
@@ -571,7 +626,8 @@ namespace {
 struct AttnPlan {
   bool mfma;
   int qtiles, splits, keys_per_split, stages;
-  int key_halves;  // waves per 16-query block, each over its share of every key tile
+  int key_halves;  // key groups: waves per query block, each over its share of every key tile
+  int qblocks;     // 16-query blocks per wave
   size_t ws;
 };
 
@@ -583,10 +639,16 @@ constexpr size_t kAttnSplitCap = 64ull << 20;  // split-KV partials never exceed
 // LDS ring (64 KB at hd 128).  Both choices come from a sweep on MI355X over
 // M = 20 .. 1024 active rows and N = 512, 1024 keys (32 heads of 128), where
 // 2 stages beat 4 at every point and more splits lost to the combine pass.
+// Measured at N = 512 .. 4096 with one workgroup per (head, 64 queries): a
+// workgroup takes ~0.9 us per 64-key tile whatever its wave layout (two
+// query blocks per wave, which halves the LDS reads, did not change it) and
+// whether 32 or 192 workgroups run, so the time is per-workgroup latency
+// rather than HBM, LDS or MFMA throughput.
 AttnPlan make_attn_plan_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits_in,
-                            int stages_in, int kh_in) {
+                            int stages_in, int kh_in, int qb_in) {
   AttnPlan p{};
-  p.key_halves = kh_in == 1 || kh_in == 2 ? kh_in : 2;
+  p.key_halves = kh_in == 1 || kh_in == 2 || kh_in == 4 ? kh_in : 2;
+  p.qblocks = qb_in == 1 || qb_in == 2 ? qb_in : 1;
   p.mfma = dtype == kBF16 && (hd == 64 || hd == 128) && nq % nkv == 0;
   p.splits = 1;
   p.keys_per_split = N;
@@ -609,50 +671,67 @@ AttnPlan make_attn_plan_cfg(int dtype, int M, int B, int N, int nq, int nkv, int
   p.splits = splits;
   const int tiles_per = (ktiles + splits - 1) / splits;
   p.keys_per_split = tiles_per * kAttnKeys;
+  // four key groups (16 waves) from 64 key tiles per workgroup on: 5-6%
+  // faster at N = 4096 unsplit, slower at N <= 1024
+  if (kh_in == 0 && tiles_per >= 64) p.key_halves = 4;
   p.stages = stages_in == 2 || stages_in == 4 ? stages_in : 2;
   p.ws = splits > 1 ? ws_of(splits) : 0;
   return p;
 }
 
 AttnPlan make_attn_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd) {
-  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, 0, 0, 0);
+  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, 0, 0, 0, 0);
 }
 
-template <int HD, bool SPLIT, int STAGES, int KH>
+template <int HD, bool SPLIT, int STAGES, int KH, int QB>
 void launch_attn_dma(dim3 grid, const void* q, const int32_t* row_start, const void* kc,
                      const void* vc, void* o, int N, int nq, int nkv, int kps, int M, float* po,
                      float* pml, hipStream_t s) {
-  constexpr size_t lds = STAGES * (size_t)(2 * kAttnKeys * HD * 2);
+  constexpr size_t ring = STAGES * (size_t)(2 * kAttnKeys * HD * 2);
+  constexpr size_t merge = attn_merge_bytes<HD, KH, QB>();
+  constexpr size_t lds = ring > merge ? ring : merge;
+  static_assert(lds <= 160 * 1024, "LDS of a CU");
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH>),
+        reinterpret_cast<const void*>(&attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH, QB>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH><<<grid, 256 * KH, lds, s>>>(
+  attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH, QB><<<grid, 64 * (4 / QB) * KH, lds, s>>>(
       (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq, nkv,
       kps, M, po, pml);
 }
 
+// Wave layouts built: (key groups, query blocks per wave) = (1, 1), (2, 1),
+// (4, 1), (2, 2), (4, 2); any other request takes (2, 1).
+template <int HD, bool SPLIT, int STAGES>
+void launch_attn_dma_layout(int kh, int qb, dim3 grid, const void* q, const int32_t* row_start,
+                            const void* kc, const void* vc, void* o, int N, int nq, int nkv,
+                            int kps, int M, float* po, float* pml, hipStream_t s) {
+#define DLM_ATTN_LAUNCH(KH, QB)                                                                \
+  launch_attn_dma<HD, SPLIT, STAGES, KH, QB>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, \
+                                             po, pml, s)
+  if (qb == 2 && kh == 4) DLM_ATTN_LAUNCH(4, 2);
+  else if (qb == 2 && kh == 2) DLM_ATTN_LAUNCH(2, 2);
+  else if (kh == 4) DLM_ATTN_LAUNCH(4, 1);
+  else if (kh == 1) DLM_ATTN_LAUNCH(1, 1);
+  else DLM_ATTN_LAUNCH(2, 1);
+#undef DLM_ATTN_LAUNCH
+}
+
 template <int HD, bool SPLIT>
-void launch_attn_kernel(dim3 grid, bool dma, int stages, int kh, const void* q,
+void launch_attn_kernel(dim3 grid, bool dma, int stages, int kh, int qb, const void* q,
                         const int32_t* row_start,
                         const void* kc, const void* vc, void* o, int N, int nq, int nkv,
                         int kps, int M, float* po, float* pml, hipStream_t s) {
   if (dma) {
-    if (stages == 2 && kh == 2)
-      launch_attn_dma<HD, SPLIT, 2, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po,
-                                         pml, s);
-    else if (stages == 2)
-      launch_attn_dma<HD, SPLIT, 2, 1>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po,
-                                         pml, s);
-    else if (kh == 2)
-      launch_attn_dma<HD, SPLIT, 4, 2>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po,
-                                         pml, s);
+    if (stages == 2)
+      launch_attn_dma_layout<HD, SPLIT, 2>(kh, qb, grid, q, row_start, kc, vc, o, N, nq, nkv, kps,
+                                           M, po, pml, s);
     else
-      launch_attn_dma<HD, SPLIT, 4, 1>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, po,
-                                         pml, s);
+      launch_attn_dma_layout<HD, SPLIT, 4>(kh, qb, grid, q, row_start, kc, vc, o, N, nq, nkv, kps,
+                                           M, po, pml, s);
   } else {
     attn_mfma_kernel<HD, SPLIT><<<grid, 256, 0, s>>>((const bf16_t*)q, row_start,
                                                      (const bf16_t*)kc, (const bf16_t*)vc,
@@ -669,16 +748,16 @@ hipError_t run_attn_mfma(const AttnPlan& p, int M, int B, int N, int nq, int nkv
   if (p.splits > 1) {
     float* po = (float*)ws;
     float* pml = po + (size_t)p.splits * M * nq * HD;
-    launch_attn_kernel<HD, true>(grid, dma, p.stages, p.key_halves, q, row_start, kc, vc, o, N, nq,
-                                 nkv, p.keys_per_split, M, po, pml, s);
+    launch_attn_kernel<HD, true>(grid, dma, p.stages, p.key_halves, p.qblocks, q, row_start, kc,
+                                 vc, o, N, nq, nkv, p.keys_per_split, M, po, pml, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t total = (size_t)M * nq * (HD / 4);
     const int gsz = (int)std::min<size_t>((total + 255) / 256, 8192);
     attn_combine_kernel<bf16_t><<<gsz, 256, 0, s>>>(po, pml, p.splits, M * nq, HD, (bf16_t*)o);
   } else {
-    launch_attn_kernel<HD, false>(grid, dma, p.stages, p.key_halves, q, row_start, kc, vc, o, N, nq,
-                                  nkv, p.keys_per_split, M, nullptr, nullptr, s);
+    launch_attn_kernel<HD, false>(grid, dma, p.stages, p.key_halves, p.qblocks, q, row_start, kc,
+                                  vc, o, N, nq, nkv, p.keys_per_split, M, nullptr, nullptr, s);
   }
   return hipGetLastError();
 }
@@ -692,9 +771,10 @@ size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int h
 hipError_t launch_attention_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd,
                                 const void* q, const int32_t* row_start, const void* kc,
                                 const void* vc, void* o, void* ws, size_t ws_bytes, int splits,
-                                int stages, int key_halves, hipStream_t s) {
+                                int stages, int key_halves, int qblocks, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  AttnPlan p = make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, stages, key_halves);
+  AttnPlan p = make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, stages, key_halves,
+                                  qblocks);
   if (p.mfma && p.ws > ws_bytes) {
     p.splits = 1;
     p.keys_per_split = N;
@@ -720,11 +800,11 @@ hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int
                             const void* q, const int32_t* row_start, const void* kc,
                             const void* vc, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
   return launch_attention_cfg(dtype, M, B, N, nq, nkv, hd, q, row_start, kc, vc, o, ws, ws_bytes,
-                              0, 0, 0, s);
+                              0, 0, 0, 0, s);
 }
 
 size_t attention_cfg_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits) {
-  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, 0, 0).ws;
+  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, 0, 0, 0).ws;
 }
 
 }  // namespace dlm

@@ -164,19 +164,40 @@ def test_attention_bf16_mfma(B, N, nq, nkv, hd, rows):
     assert (err <= 1e-2 + 2.0 ** -7 * np.abs(ref)).all(), err.max()
 
 
+ATTN_LAYOUTS = [(1, 1), (2, 1), (4, 1), (2, 2), (4, 2)]  # (key groups, query blocks per wave)
+
+
 @pytest.mark.parametrize("splits", [0, 1, 2, 3, 8, 64])
 @pytest.mark.parametrize("stages", [2, 4])
-@pytest.mark.parametrize("key_halves", [1, 2])
-def test_attention_forced_plans(splits, stages, key_halves):
+@pytest.mark.parametrize("layout", ATTN_LAYOUTS)
+def test_attention_forced_plans(splits, stages, layout):
     """Every split-KV count (including more splits than 64-key tiles, which
     the plan clamps, and a count that leaves a short last range), LDS depth
-    and number of waves per 16-query block, with two sequences of ragged row
-    counts and GQA, against the oracle."""
+    and wave layout, with two sequences of ragged row counts and GQA, against
+    the oracle."""
     B, N, nq, nkv, hd = 2, 320, 8, 2, 128
     q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, [37, 70], seed=11)
     o = ops.attention_config(_dev(q.reshape(len(rs), nq * hd)), torch.from_numpy(rst).to(DEV),
                              _dev(kc), _dev(vc.transpose(0, 1, 3, 2)), nq, nkv, hd,
-                             splits=splits, stages=stages, key_halves=key_halves)
+                             splits=splits, stages=stages, key_halves=layout[0],
+                             qblocks=layout[1])
+    ref = oracle.unit_attention(q, rs, kc, vc).reshape(len(rs), nq * hd)
+    err = np.abs(_f64(o) - ref)
+    assert (err <= 1e-2 + 2.0 ** -7 * np.abs(ref)).all(), err.max()
+
+
+@pytest.mark.parametrize("layout", ATTN_LAYOUTS)
+@pytest.mark.parametrize("B,N,nq,nkv,hd,rows", [
+    (1, 1024, 4, 4, 128, [200]),   # 16 key tiles, 4 query tiles (one partly filled)
+    (2, 256, 4, 1, 64, [100, 29]),  # hd 64, MQA: 4 queries per row share a wave
+])
+def test_attention_wave_layouts(layout, B, N, nq, nkv, hd, rows):
+    """Each wave layout without a forced split, at hd 64 and 128, against the
+    oracle."""
+    q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, rows, seed=N + hd + layout[0])
+    o = ops.attention_config(_dev(q.reshape(len(rs), nq * hd)), torch.from_numpy(rst).to(DEV),
+                             _dev(kc), _dev(vc.transpose(0, 1, 3, 2)), nq, nkv, hd, splits=1,
+                             key_halves=layout[0], qblocks=layout[1])
     ref = oracle.unit_attention(q, rs, kc, vc).reshape(len(rs), nq * hd)
     err = np.abs(_f64(o) - ref)
     assert (err <= 1e-2 + 2.0 ** -7 * np.abs(ref)).all(), err.max()
