@@ -671,9 +671,11 @@ AttnPlan make_attn_plan_cfg(int dtype, int M, int B, int N, int nq, int nkv, int
   p.splits = splits;
   const int tiles_per = (ktiles + splits - 1) / splits;
   p.keys_per_split = tiles_per * kAttnKeys;
-  // four key groups (16 waves) from 64 key tiles per workgroup on: 5-6%
-  // faster at N = 4096 unsplit, slower at N <= 1024
-  if (kh_in == 0 && tiles_per >= 64) p.key_halves = 4;
+  // four key groups (16 waves) when every workgroup runs at once on its own
+  // CU and walks at least 64 key tiles: 5-6% faster at N = 4096 with 32 or
+  // 192 workgroups, slower at N <= 1024; with many more workgroups than CUs
+  // (N = 4096 over thousands of query tiles) about 30% slower than two
+  if (kh_in == 0 && tiles_per >= 64 && busy * splits <= 256) p.key_halves = 4;
   p.stages = stages_in == 2 || stages_in == 4 ? stages_in : 2;
   p.ws = splits > 1 ? ws_of(splits) : 0;
   return p;
