@@ -30,6 +30,11 @@ _SRC = os.path.join(_HERE, "oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 POLICY = {"none": 0, "test": 1}
+SAMPLER = {"semi_ar": 0, "slowfast": 1}
+# SlowFast defaults ([SF] §4 ablation: at most 8 exploratory steps, a history
+# window of 2, variance threshold 1.0; the two confidence thresholds and k
+# are run choices)
+SF_DEFAULTS = dict(sf_k=1, sf_kmax=8, sf_whist=2, sf_tau_conv=0.9, sf_tau_high=0.9, sf_var=1.0)
 
 
 def build(force: bool = True) -> str:
@@ -59,7 +64,10 @@ class _Run(ctypes.Structure):
                 ("block_len", ctypes.c_int32), ("kl_eps", ctypes.c_double),
                 ("conf_tau", ctypes.c_double), ("n_consec", ctypes.c_int32),
                 ("kl_dir", ctypes.c_int32), ("lock_prompt_after_first_step", ctypes.c_int32),
-                ("policy", ctypes.c_int32)]
+                ("policy", ctypes.c_int32), ("sampler", ctypes.c_int32),
+                ("sf_k", ctypes.c_int32), ("sf_kmax", ctypes.c_int32),
+                ("sf_whist", ctypes.c_int32), ("sf_tau_conv", ctypes.c_double),
+                ("sf_tau_high", ctypes.c_double), ("sf_var", ctypes.c_double)]
 
 
 _PF = ctypes.POINTER(ctypes.c_float)
@@ -95,7 +103,8 @@ def lib():
             getattr(L, f).argtypes = [vp]
         L.orc_flops.argtypes = [vp]
         L.orc_flops.restype = ctypes.c_double
-        for f in ("orc_get_tokens", "orc_get_locked", "orc_get_cnt"):
+        for f in ("orc_get_tokens", "orc_get_locked", "orc_get_cnt", "orc_get_frozen",
+                  "orc_get_sf", "orc_get_has_prev"):
             getattr(L, f).argtypes = [vp, vp]
         L.orc_get_rows.argtypes = [vp, vp, vp, vp]
         L.orc_get_stats.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -115,6 +124,7 @@ def lib():
         L.orc_unit_lock_transition.argtypes = [ctypes.POINTER(_Model), ctypes.POINTER(_Run),
                                                ctypes.c_int, ctypes.c_int] + [vp] * 10
         L.orc_unit_compact.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.orc_unit_slowfast.argtypes = [ctypes.POINTER(_Run)] + [ctypes.c_int] * 3 + [vp] * 9
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -142,7 +152,8 @@ def make_run(run, lock: Dict) -> _Run:
     return _Run(run.batch, run.seq_len, run.prompt_len, run.steps, run.block_len,
                 float(lock["kl_eps"]), float(lock["conf_tau"]), int(lock["n_consec"]),
                 int(lock.get("kl_dir", 0)), int(lock["lock_prompt_after_first_step"]),
-                POLICY[lock["policy"]])
+                POLICY[lock["policy"]], SAMPLER[lock.get("sampler", "semi_ar")],
+                *[type(v)(lock.get(k, v)) for k, v in SF_DEFAULTS.items()])
 
 
 def num_threads() -> int:
@@ -247,6 +258,25 @@ class Oracle:
     def counters(self) -> np.ndarray:
         out = np.empty(self._bn(), dtype=np.int32)
         lib().orc_get_cnt(self._h, _ptr(out))
+        return out
+
+    def frozen(self) -> np.ndarray:
+        """uint8 [B][N]: positions a SlowFast accelerated stage took out of the
+        active set."""
+        out = np.empty(self._bn(), dtype=np.uint8)
+        lib().orc_get_frozen(self._h, _ptr(out))
+        return out
+
+    def has_prev(self) -> np.ndarray:
+        """uint8 [B][N]: a previous-step posterior is stored."""
+        out = np.empty(self._bn(), dtype=np.uint8)
+        lib().orc_get_has_prev(self._h, _ptr(out))
+        return out
+
+    def sf_state(self) -> np.ndarray:
+        """int32 [B][13]: phase, lo, hi, slow_n, hist_n, hist[8] per sequence."""
+        out = np.empty((self.run.batch, 13), dtype=np.int32)
+        lib().orc_get_sf(self._h, _ptr(out))
         return out
 
     def rows(self):
@@ -377,6 +407,28 @@ def unit_lock_transition(shape, run, lock, t, row_seq, row_pos, row_real, argmax
     lib().orc_unit_lock_transition(ctypes.byref(m), ctypes.byref(r), t, len(a[0]),
                                    *[_ptr(v) for v in a], _ptr(x), _ptr(locked), _ptr(cnt))
     return x, locked, cnt
+
+
+def unit_slowfast(run, lock, mask_id, pos, argmax, conf, x, frozen, has_prev, state):
+    """One SlowFast commit decision for one sequence ([SF] §2): rows (pos
+    ascending, argmax, conf) of this step; x, frozen, has_prev [N] and state
+    [13] are updated copies.  Returns (commits (pos, tok), x, frozen, has_prev,
+    state)."""
+    r = make_run(run, lock)
+    pos = np.ascontiguousarray(pos, np.int32)
+    argmax = np.ascontiguousarray(argmax, np.int32)
+    conf = _f64(conf)
+    x = np.ascontiguousarray(x, np.int32).copy()
+    frozen = np.ascontiguousarray(frozen, np.uint8).copy()
+    has_prev = np.ascontiguousarray(has_prev, np.uint8).copy()
+    state = np.ascontiguousarray(state, np.int32).copy()
+    assert state.shape == (13,) and x.shape == frozen.shape == has_prev.shape
+    cp = np.empty(max(1, len(pos)), np.int32)
+    ct = np.empty(max(1, len(pos)), np.int32)
+    n = lib().orc_unit_slowfast(ctypes.byref(r), int(mask_id), len(x), len(pos), _ptr(pos),
+                                _ptr(argmax), _ptr(conf), _ptr(x), _ptr(frozen), _ptr(has_prev),
+                                _ptr(state), _ptr(cp), _ptr(ct))
+    return (cp[:n], ct[:n]), x, frozen, has_prev, state
 
 
 def unit_compact(bits, N: int):

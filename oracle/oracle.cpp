@@ -25,6 +25,16 @@
 //  * The base sampler that unmasks tokens is confidence-ranked top-k inside
 //    semi-autoregressive blocks ([SF] §1 Problem statement names both; [SF]
 //    §2 two-stage pipeline uses top-k by confidence).
+//  * The alternative sampler is SlowFast's two-stage cycle ([SF] §2, the
+//    exploratory and accelerated stages): slow steps commit the top-k of a
+//    window while the convergence end point (the farthest still-masked
+//    position whose confidence reaches a threshold) is recorded; once the
+//    variance of its last few values falls below a threshold (or after a
+//    maximum number of slow steps) the span from the decoding frontier to
+//    that end point is fixed, fast steps commit every in-span position above
+//    a high confidence threshold (top-k when too few qualify), and the masked
+//    positions beyond the span keep their last prediction and cached K/V
+//    (they leave the active set) until the span is decoded.
 //
 // Arithmetic is fp64.  In bf16-storage mode the values the GPU engine keeps
 // in bf16 are rounded to bf16 at exactly those points (the normalised GEMM
@@ -64,6 +74,14 @@ typedef struct {
   int32_t kl_dir;  // 0: KL(p_t || p_{t-1}); 1: KL(p_{t-1} || p_t)
   int32_t lock_prompt_after_first_step;
   int32_t policy;  // 0: never lock; 1: lock test
+  // sampler 0: semi-autoregressive top-k; 1: SlowFast ([SF] §2), with k per
+  // exploratory step (also the accelerated stage's fallback), the most
+  // exploratory steps per cycle, the end points in the variance window
+  // (1..8), the convergence and in-span thresholds and sigma^2_stable; the
+  // exploratory window is block_len positions from the decoding frontier
+  int32_t sampler;
+  int32_t sf_k, sf_kmax, sf_whist;
+  double sf_tau_conv, sf_tau_high, sf_var;
 } orc_run;
 
 typedef struct {
@@ -236,6 +254,121 @@ Sched schedule(const orc_run& r, int t) {
   return out;
 }
 
+// SlowFast cycle state of one sequence.
+struct SfSeq {
+  int32_t phase = 0;       // 0: exploratory (slow), 1: accelerated (fast)
+  int32_t lo = 0, hi = 0;  // accelerated stage: the stable span [lo, hi)
+  int32_t slow_n = 0;      // exploratory steps taken in this cycle
+  int32_t hist_n = 0;      // end points recorded in this cycle (at most sf_whist kept)
+  int32_t hist[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // the kept end points, oldest first
+};
+
+// One SlowFast commit decision for one sequence ([SF] §2 two-stage pipeline).
+// Rows: this step's computed positions of the sequence (ascending), with
+// their argmax and confidence; x, frozen and has_prev are the sequence's
+// [N] arrays.  The readings where the page leaves a step open:
+//  - candidates are the computed rows still holding the mask; the decoding
+//    frontier s is the first of them;
+//  - exploratory step: the end point e = the largest candidate position
+//    whose confidence is >= sf_tau_conv is recorded (nothing is recorded
+//    when no candidate reaches it), and the stage ends when sf_whist end
+//    points are recorded and their population variance is below sf_var
+//    (compared in integers: W sum e^2 - (sum e)^2 < W^2 sf_var), or after
+//    sf_kmax exploratory steps; the span is then [s, max(e', s)] with e' the
+//    last recorded end point (s if none), and the same step already commits
+//    by the accelerated rule;
+//  - otherwise the exploratory step commits the sf_k most confident
+//    candidates in the window [s, s + block_len) (ties: smaller position);
+//  - accelerated step: every in-span candidate with confidence > sf_tau_high
+//    commits if there are at least sf_k of them, else the sf_k most
+//    confident in-span candidates do;
+//  - while in-span masks remain, masked positions at or beyond the span's
+//    end leave the active set (frozen: their last prediction and K/V stand);
+//    when the span is decoded the cycle ends, frozen positions return and,
+//    having no posterior from the step before, start without a previous
+//    posterior (no KL on their first step back).
+void slowfast_commit(const orc_run& r, int mask_id, int N, int n, const int32_t* pos,
+                     const int32_t* argmax, const double* conf, int32_t* x, uint8_t* frozen,
+                     uint8_t* has_prev, SfSeq& st, std::vector<int32_t>* cpos,
+                     std::vector<int32_t>* ctok) {
+  std::vector<int> cand;
+  for (int i = 0; i < n; ++i)
+    if (x[pos[i]] == mask_id) cand.push_back(i);
+  if (cand.empty()) return;
+  const int s = pos[cand[0]];
+  auto ahead = [&](int a, int c) {
+    if (conf[a] != conf[c]) return conf[a] > conf[c];
+    return pos[a] < pos[c];
+  };
+  auto commit = [&](int i) {
+    x[pos[i]] = argmax[i];
+    if (cpos) { cpos->push_back(pos[i]); ctok->push_back(argmax[i]); }
+  };
+  auto top_k = [&](std::vector<int> c) {
+    std::stable_sort(c.begin(), c.end(), ahead);
+    const int take = std::min<int>(r.sf_k, (int)c.size());
+    for (int j = 0; j < take; ++j) commit(c[j]);
+  };
+  const int W = r.sf_whist;
+  if (st.phase == 0) {
+    int e = -1;
+    for (int i : cand)
+      if (conf[i] >= r.sf_tau_conv) e = std::max(e, (int)pos[i]);
+    if (e >= 0) {
+      if (st.hist_n < W) {
+        st.hist[st.hist_n++] = e;
+      } else {
+        for (int j = 1; j < W; ++j) st.hist[j - 1] = st.hist[j];
+        st.hist[W - 1] = e;
+      }
+    }
+    st.slow_n += 1;
+    bool stable = false;
+    if (st.hist_n == W) {
+      long long s1 = 0, s2 = 0;
+      for (int j = 0; j < W; ++j) {
+        s1 += st.hist[j];
+        s2 += (long long)st.hist[j] * st.hist[j];
+      }
+      stable = (double)(W * s2 - s1 * s1) < (double)W * W * r.sf_var;
+    }
+    if (stable || st.slow_n >= r.sf_kmax) {
+      st.phase = 1;
+      st.lo = s;
+      st.hi = std::max(st.hist_n > 0 ? st.hist[st.hist_n - 1] : s, s) + 1;
+    } else {
+      std::vector<int> win;
+      for (int i : cand)
+        if (pos[i] < s + r.block_len) win.push_back(i);
+      top_k(win);
+      return;
+    }
+  }
+  std::vector<int> in, high;
+  for (int i : cand)
+    if (pos[i] >= st.lo && pos[i] < st.hi) in.push_back(i);
+  for (int i : in)
+    if (conf[i] > r.sf_tau_high) high.push_back(i);
+  if ((int)high.size() >= r.sf_k) {
+    for (int i : high) commit(i);
+  } else {
+    top_k(in);
+  }
+  bool left = false;
+  for (int p = st.lo; p < st.hi; ++p) left = left || x[p] == mask_id;
+  if (left) {
+    for (int i : cand)
+      if (pos[i] >= st.hi) frozen[pos[i]] = 1;
+  } else {
+    st = SfSeq{};
+    for (int p = 0; p < N; ++p)
+      if (frozen[p]) {
+        frozen[p] = 0;
+        has_prev[p] = 0;
+      }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -256,6 +389,8 @@ struct orc_state {
   std::vector<uint8_t> has_prev;   // [B][N]
   std::vector<double> kc, vc;      // [L][B][nkv][N][hd]
   std::vector<double> prevlogp;    // [B][N][V]
+  std::vector<uint8_t> frozen;     // [B][N] out of the active set during an accelerated stage
+  std::vector<SfSeq> sf;           // [B] SlowFast cycle state
 
   // results of the last step (rows in (b, pos) ascending order)
   bool stepped = false, partial = false;
@@ -286,9 +421,28 @@ void lock_transition(const orc_model& m, const orc_run& r, int t, int M,
                      const int32_t* argmax, const double* conf, const double* kl,
                      const uint8_t* has_kl, int32_t* x, uint8_t* locked, int32_t* cnt,
                      std::vector<int32_t>* cseq, std::vector<int32_t>* cpos,
-                     std::vector<int32_t>* ctok, bool do_commit = true, bool do_lock = true) {
+                     std::vector<int32_t>* ctok, bool do_commit = true, bool do_lock = true,
+                     SfSeq* sf = nullptr, uint8_t* frozen = nullptr,
+                     uint8_t* has_prev = nullptr) {
   const int N = r.seq_len;
-  const Sched sc = do_commit ? schedule(r, t) : Sched{-1, 0, 0, 0};
+  const bool slowfast = r.sampler == 1;
+  const Sched sc = do_commit && !slowfast ? schedule(r, t) : Sched{-1, 0, 0, 0};
+  if (do_commit && slowfast && sf) {
+    // rows are in ascending (sequence, position) order: one contiguous run
+    // per sequence
+    int i0 = 0;
+    for (int b = 0; b < r.batch; ++b) {
+      int i1 = i0;
+      while (i1 < M && row_seq[i1] == b) ++i1;
+      std::vector<int32_t> bp, bt;
+      slowfast_commit(r, m.mask_id, N, i1 - i0, row_pos + i0, argmax + i0, conf + i0,
+                      x + (size_t)b * N, frozen + (size_t)b * N, has_prev + (size_t)b * N, sf[b],
+                      &bp, &bt);
+      for (size_t j = 0; j < bp.size(); ++j)
+        if (cseq) { cseq->push_back(b); cpos->push_back(bp[j]); ctok->push_back(bt[j]); }
+      i0 = i1;
+    }
+  }
   // Commit: among this step's rows whose token is still the mask and which
   // lie in the current block, the k most confident take their argmax
   // (ties: smaller position first).
@@ -338,7 +492,8 @@ orc_state* orc_create(const orc_model* m, const orc_weights* w, const orc_run* r
   if (!m || !w || !r || !prompts) return nullptr;
   if (r->batch <= 0 || r->seq_len <= 0 || r->prompt_len < 0 || r->prompt_len > r->seq_len ||
       r->steps <= 0 || r->block_len <= 0 || m->n_heads % m->n_kv_heads != 0 ||
-      m->head_dim % 2 != 0)
+      m->head_dim % 2 != 0 || (r->sampler != 0 && r->sampler != 1) ||
+      (r->sampler == 1 && (r->sf_k < 1 || r->sf_kmax < 1 || r->sf_whist < 1 || r->sf_whist > 8)))
     return nullptr;
   orc_state* s = new orc_state();
   s->m = *m;
@@ -362,6 +517,8 @@ orc_state* orc_create(const orc_model* m, const orc_weights* w, const orc_run* r
   s->locked.assign(BN, 0);
   s->cnt.assign(BN, 0);
   s->has_prev.assign(BN, 0);
+  s->frozen.assign(BN, 0);
+  s->sf.assign(r->batch, SfSeq{});
   const size_t kvn = (size_t)L * BN * m->n_kv_heads * m->head_dim;
   s->kc.assign(kvn, 0.0);
   s->vc.assign(kvn, 0.0);
@@ -383,13 +540,14 @@ int orc_step_sample(orc_state* s, const int32_t* sample_rows, int n_sample) {
   const int N = r.seq_len, d = m.d_model, hd = m.head_dim, nq = m.n_heads, nkv = m.n_kv_heads;
   const int dff = m.d_ff, V = m.vocab, qo = nq * hd, qkv_out = (nq + 2 * nkv) * hd;
 
-  // Active set: every unlocked position, ascending ([SL] §2 permanent deactivation).
+  // Active set: every unlocked position, ascending ([SL] §2 permanent
+  // deactivation), less the positions a SlowFast accelerated stage froze.
   s->row_seq.clear();
   s->row_pos.clear();
   s->row_real.clear();
   for (int b = 0; b < r.batch; ++b)
     for (int i = 0; i < N; ++i)
-      if (!s->locked[(size_t)b * N + i]) {
+      if (!s->locked[(size_t)b * N + i] && !s->frozen[(size_t)b * N + i]) {
         s->row_seq.push_back(b);
         s->row_pos.push_back(i);
         s->row_real.push_back(s->x[(size_t)b * N + i] != m.mask_id);
@@ -534,7 +692,8 @@ int orc_lock_update(orc_state* s, const int32_t* ov_commit_seq, const int32_t* o
   lock_transition(s->m, r, s->t, s->M, s->row_seq.data(), s->row_pos.data(), s->row_real.data(),
                   s->row_argmax.data(), s->row_conf.data(), s->row_kl.data(),
                   s->row_has_kl.data(), s->x.data(), s->locked.data(), s->cnt.data(),
-                  &s->commit_seq, &s->commit_pos, &s->commit_tok, !ov_commit, !ov_lock);
+                  &s->commit_seq, &s->commit_pos, &s->commit_tok, !ov_commit, !ov_lock,
+                  s->sf.data(), s->frozen.data(), s->has_prev.data());
   if (ov_commit) {
     s->commit_seq.assign(ov_commit_seq, ov_commit_seq + n_ov_commit);
     s->commit_pos.assign(ov_commit_pos, ov_commit_pos + n_ov_commit);
@@ -559,6 +718,21 @@ double orc_flops(const orc_state* s) { return s->flops; }
 void orc_get_tokens(const orc_state* s, int32_t* out) { std::copy(s->x.begin(), s->x.end(), out); }
 void orc_get_locked(const orc_state* s, uint8_t* out) { std::copy(s->locked.begin(), s->locked.end(), out); }
 void orc_get_cnt(const orc_state* s, int32_t* out) { std::copy(s->cnt.begin(), s->cnt.end(), out); }
+void orc_get_has_prev(const orc_state* s, uint8_t* out) {
+  std::copy(s->has_prev.begin(), s->has_prev.end(), out);
+}
+void orc_get_frozen(const orc_state* s, uint8_t* out) {
+  std::copy(s->frozen.begin(), s->frozen.end(), out);
+}
+// SlowFast state per sequence: phase, lo, hi, slow_n, hist_n, hist[8]
+void orc_get_sf(const orc_state* s, int32_t* out /* [B][13] */) {
+  for (size_t b = 0; b < s->sf.size(); ++b) {
+    const SfSeq& q = s->sf[b];
+    int32_t* o = out + b * 13;
+    o[0] = q.phase; o[1] = q.lo; o[2] = q.hi; o[3] = q.slow_n; o[4] = q.hist_n;
+    for (int j = 0; j < 8; ++j) o[5 + j] = q.hist[j];
+  }
+}
 void orc_get_rows(const orc_state* s, int32_t* seq, int32_t* pos, uint8_t* real) {
   std::copy(s->row_seq.begin(), s->row_seq.end(), seq);
   std::copy(s->row_pos.begin(), s->row_pos.end(), pos);
@@ -648,6 +822,26 @@ int orc_unit_lock_transition(const orc_model* m, const orc_run* r, int t, int M,
   lock_transition(*m, *r, t, M, row_seq, row_pos, row_real, argmax, conf, kl, has_kl, x, locked,
                   cnt, nullptr, nullptr, nullptr);
   return 0;
+}
+// One SlowFast commit decision for one sequence on given rows; state
+// [13] = phase, lo, hi, slow_n, hist_n, hist[8] in and out; commits (at most
+// n) written to commit_pos / commit_tok, their count returned.
+int orc_unit_slowfast(const orc_run* r, int mask_id, int N, int n, const int32_t* pos,
+                      const int32_t* argmax, const double* conf, int32_t* x, uint8_t* frozen,
+                      uint8_t* has_prev, int32_t* state, int32_t* commit_pos,
+                      int32_t* commit_tok) {
+  SfSeq st;
+  st.phase = state[0]; st.lo = state[1]; st.hi = state[2]; st.slow_n = state[3];
+  st.hist_n = state[4];
+  for (int j = 0; j < 8; ++j) st.hist[j] = state[5 + j];
+  std::vector<int32_t> cp, ct;
+  slowfast_commit(*r, mask_id, N, n, pos, argmax, conf, x, frozen, has_prev, st, &cp, &ct);
+  state[0] = st.phase; state[1] = st.lo; state[2] = st.hi; state[3] = st.slow_n;
+  state[4] = st.hist_n;
+  for (int j = 0; j < 8; ++j) state[5 + j] = st.hist[j];
+  std::copy(cp.begin(), cp.end(), commit_pos);
+  std::copy(ct.begin(), ct.end(), commit_tok);
+  return (int)cp.size();
 }
 // Active set from a bitmask: rows (b, pos) with bit clear, ascending.
 int orc_unit_compact(const uint64_t* bits, int B, int N, int32_t* row_seq, int32_t* row_pos,

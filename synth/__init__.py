@@ -75,6 +75,12 @@ LOCK_SETTINGS = {
                       n_consec=2, lock_prompt_after_first_step=1),
     "vanilla": dict(policy="none", kl_eps=-1.0, conf_tau=0.0, n_consec=2,
                     lock_prompt_after_first_step=0),
+    # the natural lock test with the SlowFast sampler ([SF] §2) in place of the
+    # semi-autoregressive block schedule; thresholds at the pages' 0.9, the
+    # stage limits of [SF] §4 (8 exploratory steps, window 2, variance 1.0)
+    "slowfast": dict(policy="test", kl_eps=1e-3, conf_tau=0.9, n_consec=2,
+                     lock_prompt_after_first_step=1, sampler="slowfast", sf_k=3, sf_kmax=8,
+                     sf_whist=2, sf_tau_conv=0.9, sf_tau_high=0.9, sf_var=1.0),
 }
 
 

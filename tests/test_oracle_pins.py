@@ -427,3 +427,138 @@ def test_linear_and_compact_primitives():
         bb, ii = np.nonzero(~dense)
         assert np.array_equal(seq, bb) and np.array_equal(pos, ii)
         assert np.array_equal(mb, (~dense).sum(axis=1))
+
+
+# --- SlowFast sampler ([SF] §2 two-stage pipeline) ------------------------------
+# Hand-worked cycles: each expected commit, span and state below follows from
+# the page's description (exploratory top-k in a window while the end point's
+# variance is tracked, accelerated in-span threshold commits with a top-k
+# fallback, out-of-span positions frozen until the span is decoded).
+
+SF_MASK = 99
+
+
+def _sf_run(N=16, window=4):
+    return synth.RunShape(1, N, 4, 16, window)
+
+
+def _sf_lock(**kw):
+    d = dict(synth.LOCK_SETTINGS["scheduled"], sampler="slowfast", sf_k=1, sf_kmax=8,
+             sf_whist=2, sf_tau_conv=0.5, sf_tau_high=0.8, sf_var=1.0)
+    d.update(kw)
+    return d
+
+
+def _sf_step(run, lock, x, frozen, hp, st, conf_of):
+    """Rows = every non-frozen position (ascending); argmax of position p is
+    1000 + p; conf from conf_of (default 0.1)."""
+    pos = np.array([p for p in range(len(x)) if not frozen[p]], np.int32)
+    conf = np.array([conf_of.get(int(p), 0.1) for p in pos])
+    (cp, ct), x, frozen, hp, st = oracle.unit_slowfast(run, lock, SF_MASK, pos, 1000 + pos, conf,
+                                                       x, frozen, hp, st)
+    assert np.array_equal(ct, 1000 + cp)
+    return sorted(cp.tolist()), x, frozen, hp, st
+
+
+def test_slowfast_cycle_hand_worked():
+    run, lock = _sf_run(), _sf_lock()
+    x = np.array([1, 2, 3, 4] + [SF_MASK] * 12, np.int32)
+    frozen = np.zeros(16, np.uint8)
+    hp = np.ones(16, np.uint8)
+    st = np.zeros(13, np.int32)
+    # exploratory: frontier 4, end point 8 (positions 5 and 8 reach 0.5), one
+    # end point recorded; top-1 of the window [4, 8) is position 5
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st,
+                                    {4: 0.3, 5: 0.6, 6: 0.2, 8: 0.55})
+    assert c == [5] and list(st[:5]) == [0, 0, 0, 1, 1] and st[5] == 8
+    # end point 9: variance of (8, 9) = 0.25 < 1 -> span [4, 10); position 4
+    # alone is above 0.8 and k = 1 -> it commits; 10..15 freeze
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {4: 0.85, 9: 0.7})
+    assert c == [4] and list(st[:5]) == [1, 4, 10, 2, 2] and list(st[5:7]) == [8, 9]
+    assert frozen.tolist() == [0] * 10 + [1] * 6
+    # accelerated: 6 and 7 above 0.8 both commit; 8, 9 left
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st,
+                                    {6: 0.9, 7: 0.95, 8: 0.3, 9: 0.1})
+    assert c == [6, 7] and st[0] == 1
+    # none above 0.8: top-1 fallback (position 9, 0.45)
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {8: 0.4, 9: 0.45})
+    assert c == [9] and st[0] == 1 and frozen[10:].all()
+    # last in-span mask: the cycle ends, the frozen positions return without a
+    # previous posterior, the state resets
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {8: 0.2})
+    assert c == [8] and not st.any() and not frozen.any()
+    assert hp.tolist() == [1] * 10 + [0] * 6
+    # a new cycle from frontier 10: nothing reaches 0.5 -> no end point
+    # recorded; top-1 of [10, 14) is 12
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {12: 0.45, 15: 0.49})
+    assert c == [12] and list(st[:5]) == [0, 0, 0, 1, 0]
+    assert (x[:10] != SF_MASK).all() and x[12] == 1012
+
+
+def test_slowfast_kmax_and_empty_span():
+    """End points too scattered for the variance test: the stage ends after
+    sf_kmax exploratory steps; with no converged position the span is the
+    frontier alone."""
+    run, lock = _sf_run(N=24, window=8), _sf_lock(sf_kmax=3, sf_k=2)
+    x = np.array([1, 2, 3, 4] + [SF_MASK] * 20, np.int32)
+    frozen, hp, st = np.zeros(24, np.uint8), np.ones(24, np.uint8), np.zeros(13, np.int32)
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {20: 0.6, 6: 0.4, 7: 0.3})
+    assert c == [6, 7] and st[0] == 0 and st[5] == 20
+    # the window [4, 12) holds position 10 (0.6) and 5 (0.3): top-2
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {10: 0.6, 4: 0.2, 5: 0.3})
+    assert c == [5, 10] and st[0] == 0 and list(st[5:7]) == [20, 10]  # variance 25
+    # third exploratory step: no position reaches 0.5 -> nothing recorded;
+    # sf_kmax reached -> span [4, 11) up to the last end point (10); no
+    # in-span position above 0.8 -> top-2 of the span: 9 (0.45) and 4 (0.1,
+    # smallest position among the rest); 11.. freeze
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {9: 0.45})
+    assert c == [4, 9] and list(st[:5]) == [1, 4, 11, 3, 2]
+    assert frozen.tolist() == [0] * 11 + [1] * 13
+
+
+def test_slowfast_kmax_without_end_point():
+    """No position ever reaches the convergence threshold: the stage ends by
+    sf_kmax with the frontier alone as the span, decoded at once."""
+    run, lock = _sf_run(N=12, window=2), _sf_lock(sf_kmax=2)
+    x = np.array([1, 2, 3, 4] + [SF_MASK] * 8, np.int32)
+    frozen, hp, st = np.zeros(12, np.uint8), np.ones(12, np.uint8), np.zeros(13, np.int32)
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {5: 0.3})
+    assert c == [5] and list(st[:5]) == [0, 0, 0, 1, 0]
+    c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {7: 0.3})
+    assert c == [4] and not st.any() and not frozen.any()
+
+
+def test_slowfast_variance_test_against_numpy():
+    """The stage-end test against numpy's population variance of the last
+    sf_whist end points, on random end-point sequences (W = 1..4)."""
+    rng = np.random.default_rng(5)
+    for W in (1, 2, 3, 4):
+        for trial in range(40):
+            var_thr = float(rng.choice([0.5, 1.0, 2.0, 6.25]))
+            lock = _sf_lock(sf_whist=W, sf_kmax=100, sf_var=var_thr)
+            N = 64
+            run = _sf_run(N=N, window=1)
+            x = np.array([1, 2, 3, 4] + [SF_MASK] * (N - 4), np.int32)
+            frozen, hp, st = np.zeros(N, np.uint8), np.ones(N, np.uint8), np.zeros(13, np.int32)
+            ends = []
+            for step in range(6):
+                s = int(np.argmax(x == SF_MASK))
+                e = int(rng.integers(s, min(N, s + 6)))
+                ends.append(e)
+                # only position e reaches tau_conv, below tau_high; the window of
+                # one position commits the frontier while exploring
+                c, x, frozen, hp, st = _sf_step(run, lock, x, frozen, hp, st, {e: 0.6})
+                last = ends[-W:]
+                stable = len(ends) >= W and np.var(np.array(last, np.float64)) < var_thr
+                if stable:
+                    assert st[0] == 1 or (not st.any()), (W, ends)
+                    break
+                assert st[0] == 0 and c == [s], (W, ends, st)
+
+
+def test_slowfast_ties_prefer_smaller_position():
+    run, lock = _sf_run(), _sf_lock(sf_k=2)
+    x = np.array([1, 2, 3, 4] + [SF_MASK] * 12, np.int32)
+    frozen, hp, st = np.zeros(16, np.uint8), np.ones(16, np.uint8), np.zeros(13, np.int32)
+    c, *_ = _sf_step(run, lock, x, frozen, hp, st, {4: 0.3, 5: 0.4, 6: 0.4, 7: 0.4})
+    assert c == [5, 6]
