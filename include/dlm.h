@@ -50,6 +50,7 @@ enum {
 
 enum { DLM_FP32 = 0, DLM_BF16 = 1 };
 enum { DLM_LOCK_NONE = 0, DLM_LOCK_TEST = 1 };
+enum { DLM_SAMPLER_SEMI_AR = 0, DLM_SAMPLER_SLOWFAST = 1 };
 
 /* Model shape.  Pre-RMSNorm bidirectional transformer, SwiGLU FFN, untied LM
  * head, no biases, rotary embedding with half-split pairs (component j with
@@ -89,15 +90,36 @@ typedef struct {
  * token this step was real: pass = KL defined && KL <= kl_eps && conf >=
  * conf_tau; a counter of consecutive passes locks the position at n_consec.
  * KL is KL(p_t || p_{t-1}) (kl_dir 0) or KL(p_{t-1} || p_t) (kl_dir 1).  With
- * lock_prompt_after_first_step, every prompt position locks after step 0. */
+ * lock_prompt_after_first_step, every prompt position locks after step 0.
+ *
+ * sampler DLM_SAMPLER_SLOWFAST replaces the block schedule by SlowFast's
+ * two-stage cycle (SlowFast page, §2 two-stage pipeline; the page's §4
+ * ablation settles on sf_kmax 8, sf_whist 2, sf_var 1.0), per sequence.
+ * Candidates are the step's active positions still holding the mask; the
+ * frontier s is the first.  Exploratory step: the end point (largest
+ * candidate position with conf >= sf_tau_conv; none if no candidate reaches
+ * it) is recorded; the stage ends when sf_whist (1..8) end points are
+ * recorded and their population variance is below sf_var, or after sf_kmax
+ * exploratory steps, fixing the span [s, max(last end point, s)]; otherwise
+ * the sf_k most confident candidates of [s, s + block_len) commit.
+ * Accelerated step (also the step that fixed the span): every in-span
+ * candidate with conf > sf_tau_high commits when at least sf_k do, else the
+ * sf_k most confident in-span candidates; while in-span masks remain, the
+ * masked positions beyond the span leave the active set (frozen: their K/V
+ * and last prediction stand), and once the span is decoded they return
+ * without a previous posterior (no KL on their first step back) and a new
+ * cycle starts.  The other sf_ fields are ignored for the semi-AR sampler. */
 typedef struct {
   int32_t batch, seq_len, prompt_len, steps, block_len;
   float kl_eps, conf_tau;
   int32_t n_consec, kl_dir, lock_prompt_after_first_step, lock_policy;
+  int32_t sampler, sf_k, sf_kmax, sf_whist;
+  float sf_tau_conv, sf_tau_high, sf_var;
 } dlm_run_desc;
 
 /* Replay override for dlm_lock_update (host pointers).  n_commit >= 0 replaces
- * the top-k choice by the listed (seq, pos, tok) commits; lock_bits non-null
+ * the top-k choice by the listed (seq, pos, tok) commits (with the SlowFast
+ * sampler the cycle state and frozen set are then left as they were); lock_bits non-null
  * replaces the lock test: bits |= lock_bits ([batch][ceil(seq_len/64)]) and
  * the counters are set from counters ([batch][seq_len]) when non-null, else
  * kept. */
@@ -157,7 +179,12 @@ enum {
   DLM_GET_LOGITS = 10,   /* float  [batch][seq_len][vocab]; rows of this step's active positions */
   DLM_GET_ROW_REAL = 11, /* int32  [M] input token was not the mask */
   DLM_GET_KCACHE = 12,   /* dtype  [L][batch][n_kv_heads][seq_len][head_dim] */
-  DLM_GET_VCACHE = 13    /* dtype  [L][batch][n_kv_heads][head_dim][seq_len] (transposed) */
+  DLM_GET_VCACHE = 13,   /* dtype  [L][batch][n_kv_heads][head_dim][seq_len] (transposed) */
+  DLM_GET_FROZEN = 14,   /* uint64 [batch][ceil(seq_len/64)] SlowFast out-of-span positions */
+  DLM_GET_SF_STATE = 15, /* int32  [batch][16] SlowFast cycle: phase (0 exploratory, 1
+                            accelerated), span lo, span hi (exclusive), exploratory steps,
+                            recorded end points n, the last n end points (up to 8), 3 unused */
+  DLM_GET_HAS_PREV = 16  /* int32  [batch][seq_len] a previous-step posterior is stored */
 };
 int dlm_get(dlm_handle* h, int32_t what, const void** dev_ptr, int64_t* n);
 

@@ -202,6 +202,24 @@ int dlm_op_commit_lock(int32_t batch, int32_t seq_len, int32_t prompt_len, int32
                        const float* kl, const int32_t* has_kl, int32_t* tokens,
                        uint64_t* bits, int32_t* counters, void* stream);
 
+/* One SlowFast commit decision per sequence (SlowFast page, §2 two-stage
+ * pipeline; the rule dlm_run_desc documents for DLM_SAMPLER_SLOWFAST, with
+ * window = the exploratory window, block_len there), as dlm_lock_update runs
+ * it, without the lock test.  Device arrays: the step's rows (row_pos,
+ * argmax, conf [M], sequences delimited by row_start [batch+1]); tokens
+ * [batch][seq_len] (commits written), frozen bits uint64
+ * [batch][ceil(seq_len/64)], has_prev int32 [batch][seq_len] (cleared for
+ * the positions a finished cycle unfreezes) and the cycle state int32
+ * [batch][16] (phase, lo, hi, exploratory steps, end points recorded, end
+ * points[8], unused[3]; all zero at the start) are updated in place.
+ * seq_len <= 4096 (the candidates are staged in LDS), else DLM_E_INVALID. */
+int dlm_op_slowfast_commit(int32_t batch, int32_t seq_len, int32_t mask_id, int32_t window,
+                           int32_t sf_k, int32_t sf_kmax, int32_t sf_whist, float sf_tau_conv,
+                           float sf_tau_high, float sf_var, const int32_t* row_pos,
+                           const int32_t* row_start, const int32_t* argmax, const float* conf,
+                           int32_t* tokens, uint64_t* frozen, int32_t* has_prev,
+                           int32_t* sf_state, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

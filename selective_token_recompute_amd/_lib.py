@@ -16,9 +16,12 @@ DLM_OK, DLM_E_INVALID, DLM_E_SIZE, DLM_E_HIP, DLM_E_STATE, DLM_E_UNSUPPORTED, DL
     0, -1, -2, -3, -4, -5, -6)
 DLM_FP32, DLM_BF16 = 0, 1
 DLM_LOCK_NONE, DLM_LOCK_TEST = 0, 1
+DLM_SAMPLER_SEMI_AR, DLM_SAMPLER_SLOWFAST = 0, 1
 (DLM_GET_TOKENS, DLM_GET_LOCK_BITS, DLM_GET_COUNTERS, DLM_GET_ROW_SEQ, DLM_GET_ROW_POS,
  DLM_GET_ARGMAX, DLM_GET_CONF, DLM_GET_KL, DLM_GET_HAS_KL, DLM_GET_LSE, DLM_GET_LOGITS,
- DLM_GET_ROW_REAL, DLM_GET_KCACHE, DLM_GET_VCACHE) = range(14)
+ DLM_GET_ROW_REAL, DLM_GET_KCACHE, DLM_GET_VCACHE, DLM_GET_FROZEN, DLM_GET_SF_STATE,
+ DLM_GET_HAS_PREV) = range(17)
+SF_STATE_INTS = 16
 KCLASSES = ["compact", "embed_norm", "rmsnorm", "gemm_qkv", "rope_kv", "attention", "gemm_o",
             "gemm_gate_up", "gemm_down", "gemm_lm_head", "vocab_stats", "commit_lock"]
 DLM_EPI_STORE_F32, DLM_EPI_RESID_ADD, DLM_EPI_SWIGLU, DLM_EPI_LOGITS = 0, 1, 2, 3
@@ -33,7 +36,7 @@ EXPORTS = [
     "dlm_op_attention_ws_bytes", "dlm_op_attention", "dlm_op_attention_config_ws_bytes",
     "dlm_op_attention_config", "dlm_op_vocab_ws_bytes",
     "dlm_op_vocab_stats", "dlm_op_lm_head_stats_ws_bytes", "dlm_op_lm_head_stats",
-    "dlm_op_commit_lock",
+    "dlm_op_commit_lock", "dlm_op_slowfast_commit",
 ]
 
 i32 = ctypes.c_int32
@@ -59,7 +62,9 @@ class dlm_weights(ctypes.Structure):
 class dlm_run_desc(ctypes.Structure):
     _fields_ = [("batch", i32), ("seq_len", i32), ("prompt_len", i32), ("steps", i32),
                 ("block_len", i32), ("kl_eps", f32), ("conf_tau", f32), ("n_consec", i32),
-                ("kl_dir", i32), ("lock_prompt_after_first_step", i32), ("lock_policy", i32)]
+                ("kl_dir", i32), ("lock_prompt_after_first_step", i32), ("lock_policy", i32),
+                ("sampler", i32), ("sf_k", i32), ("sf_kmax", i32), ("sf_whist", i32),
+                ("sf_tau_conv", f32), ("sf_tau_high", f32), ("sf_var", f32)]
 
 
 class dlm_override(ctypes.Structure):
@@ -127,6 +132,7 @@ def lib() -> ctypes.CDLL:
         L.dlm_op_lm_head_stats.argtypes = ([i32] * 3 + [vp] * 5 + [i32] * 3 + [vp] * 10 +
                                            [i32, vp, sz, vp])
         L.dlm_op_commit_lock.argtypes = ([i32] * 10 + [f32, f32, i32, i32] + [vp] * 11 + [vp])
+        L.dlm_op_slowfast_commit.argtypes = [i32] * 7 + [f32] * 3 + [vp] * 9
         _lib = L
     return _lib
 

@@ -33,6 +33,7 @@ inline size_t al(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Offsets of every array inside state_mem.
 struct Layout {
   size_t tokens, bits, counters, has_prev, row_seq, row_pos, m_b, row_start, ctl, row_real;
+  size_t frozen, sf_state;
   size_t argmax, conf, kl, has_kl, lse_row, lse[2], z[2], kc, vc, rope, h, a, qkv, q, o, u;
   size_t ws, ws_bytes, ov_cseq, ov_cpos, ov_ctok, ov_bits, ov_cnt, total;
 };
@@ -64,6 +65,11 @@ bool valid_run(const dlm_run_desc* r) {
   if ((int64_t)r->batch * r->seq_len > (1 << 24)) return false;
   if (n_blocks(r) > r->steps) return false;
   if (std::isnan(r->kl_eps) || std::isnan(r->conf_tau)) return false;
+  if (r->sampler != DLM_SAMPLER_SEMI_AR && r->sampler != DLM_SAMPLER_SLOWFAST) return false;
+  if (r->sampler == DLM_SAMPLER_SLOWFAST &&
+      (r->seq_len > 4096 || r->sf_k < 1 || r->sf_kmax < 1 || r->sf_whist < 1 || r->sf_whist > 8 ||
+       std::isnan(r->sf_tau_conv) || std::isnan(r->sf_tau_high) || std::isnan(r->sf_var)))
+    return false;
   return true;
 }
 
@@ -100,6 +106,8 @@ Layout make_layout(const dlm_model_desc& m, const dlm_run_desc& r) {
   };
   L.tokens = take(BN * 4);
   L.bits = take(B * W * 8);
+  L.frozen = take(B * W * 8);
+  L.sf_state = take(B * kSfStateInts * 4);
   L.counters = take(BN * 4);
   L.has_prev = take(BN * 4);
   L.row_seq = take(BN * 4);
@@ -310,7 +318,8 @@ int dlm_step_init(const dlm_model_desc* model, const dlm_weights* w, const dlm_r
   hipError_t e = launch_init_state(B, N, run->prompt_len, model->mask_id, prompt_tokens,
                                    h->at<int32_t>(lay.tokens), h->at<uint64_t>(lay.bits),
                                    h->at<int32_t>(lay.counters), h->at<int32_t>(lay.has_prev),
-                                   h->at<int32_t>(lay.ctl), h->stream);
+                                   h->at<int32_t>(lay.ctl), h->at<uint64_t>(lay.frozen),
+                                   h->at<int32_t>(lay.sf_state), h->stream);
   if (e == hipSuccess && model->rope_base > 0.f)
     e = launch_rope_table(N, model->head_dim, model->rope_base, h->at<float>(lay.rope), h->stream);
   if (e != hipSuccess) {
@@ -338,8 +347,9 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out) {
   int32_t* row_start = h->at<int32_t>(y.row_start);
   int32_t* ctl = h->at<int32_t>(y.ctl);
   TRY(timed(h, DLM_K_COMPACT, B * ((N + 63) / 64) * 8.0, 0.0, [&] {
-    return launch_compact(h->at<uint64_t>(y.bits), B, N, row_seq, row_pos, h->at<int32_t>(y.m_b),
-                          row_start, ctl, s);
+    return launch_compact(h->at<uint64_t>(y.bits),
+                          r.sampler == DLM_SAMPLER_SLOWFAST ? h->at<uint64_t>(y.frozen) : nullptr,
+                          B, N, row_seq, row_pos, h->at<int32_t>(y.m_b), row_start, ctl, s);
   }));
   int32_t hctl[2] = {0, 0};
   TRY(hipMemcpyAsync(hctl, ctl, sizeof(hctl), hipMemcpyDeviceToHost, s));
@@ -513,6 +523,17 @@ int dlm_lock_update(dlm_handle* h, const dlm_override* ov) {
   la.tokens = h->at<int32_t>(y.tokens);
   la.bits = h->at<uint64_t>(y.bits);
   la.counters = h->at<int32_t>(y.counters);
+  la.sampler = r.sampler;
+  la.sf_window = r.block_len;
+  la.sf_k = r.sf_k;
+  la.sf_kmax = r.sf_kmax;
+  la.sf_whist = r.sf_whist;
+  la.sf_tau_conv = r.sf_tau_conv;
+  la.sf_tau_high = r.sf_tau_high;
+  la.sf_var = r.sf_var;
+  la.frozen = h->at<uint64_t>(y.frozen);
+  la.has_prev = h->at<int32_t>(y.has_prev);
+  la.sf_state = h->at<int32_t>(y.sf_state);
   if (la.do_commit || la.do_lock)
     TRY(timed(h, DLM_K_COMMIT_LOCK, 0.0, 0.0, [&] { return launch_commit_lock(la, h->stream); }));
   if (ov && (ov_commit || ov_lock)) {
@@ -570,6 +591,9 @@ int dlm_get(dlm_handle* h, int32_t what, const void** dev_ptr, int64_t* n) {
     case DLM_GET_ROW_REAL: off = y.row_real; cnt = M; break;
     case DLM_GET_KCACHE: off = y.kc; cnt = kvn; break;
     case DLM_GET_VCACHE: off = y.vc; cnt = kvn; break;
+    case DLM_GET_FROZEN: off = y.frozen; cnt = B * ((N + 63) / 64); break;
+    case DLM_GET_SF_STATE: off = y.sf_state; cnt = B * kSfStateInts; break;
+    case DLM_GET_HAS_PREV: off = y.has_prev; cnt = BN; break;
     default: return DLM_E_INVALID;
   }
   *dev_ptr = h->base + off;
@@ -630,8 +654,8 @@ int dlm_op_compact(const uint64_t* bits, int32_t batch, int32_t seq_len, int32_t
   if (!bits || !row_seq || !row_pos || !m_b || !row_start || !ctl) return DLM_E_INVALID;
   if (batch < 1 || batch > 1024 || seq_len < 1 || (int64_t)batch * seq_len > (1 << 24))
     return DLM_E_INVALID;
-  return hip_status(launch_compact(bits, batch, seq_len, row_seq, row_pos, m_b, row_start, ctl,
-                                   (hipStream_t)stream));
+  return hip_status(launch_compact(bits, nullptr, batch, seq_len, row_seq, row_pos, m_b,
+                                   row_start, ctl, (hipStream_t)stream));
 }
 
 int dlm_op_embed_rmsnorm(int32_t dtype, int32_t M, int32_t d, int32_t seq_len, float eps,
@@ -855,6 +879,43 @@ int dlm_op_commit_lock(int32_t batch, int32_t seq_len, int32_t prompt_len, int32
   LockArgs la{batch, seq_len, prompt_len, mask_id, blk_lo, blk_hi, k, do_commit, do_lock,
               policy, kl_eps, conf_tau, n_consec, lock_prompt, row_seq, row_pos, row_start,
               row_real, argmax, conf, kl, has_kl, tokens, bits, counters};
+  return hip_status(launch_commit_lock(la, (hipStream_t)stream));
+}
+
+int dlm_op_slowfast_commit(int32_t batch, int32_t seq_len, int32_t mask_id, int32_t window,
+                           int32_t sf_k, int32_t sf_kmax, int32_t sf_whist, float sf_tau_conv,
+                           float sf_tau_high, float sf_var, const int32_t* row_pos,
+                           const int32_t* row_start, const int32_t* argmax, const float* conf,
+                           int32_t* tokens, uint64_t* frozen, int32_t* has_prev,
+                           int32_t* sf_state, void* stream) {
+  if (batch < 1 || batch > 1024 || seq_len < 1 || seq_len > 4096 || window < 1 || sf_k < 1 ||
+      sf_kmax < 1 || sf_whist < 1 || sf_whist > 8 || std::isnan(sf_tau_conv) ||
+      std::isnan(sf_tau_high) || std::isnan(sf_var))
+    return DLM_E_INVALID;
+  if (!row_pos || !row_start || !argmax || !conf || !tokens || !frozen || !has_prev || !sf_state)
+    return DLM_E_INVALID;
+  LockArgs la{};
+  la.B = batch;
+  la.N = seq_len;
+  la.mask_id = mask_id;
+  la.do_commit = 1;
+  la.do_lock = 0;
+  la.row_pos = row_pos;
+  la.row_start = row_start;
+  la.argmax = argmax;
+  la.conf = conf;
+  la.tokens = tokens;
+  la.sampler = DLM_SAMPLER_SLOWFAST;
+  la.sf_window = window;
+  la.sf_k = sf_k;
+  la.sf_kmax = sf_kmax;
+  la.sf_whist = sf_whist;
+  la.sf_tau_conv = sf_tau_conv;
+  la.sf_tau_high = sf_tau_high;
+  la.sf_var = sf_var;
+  la.frozen = frozen;
+  la.has_prev = has_prev;
+  la.sf_state = sf_state;
   return hip_status(launch_commit_lock(la, (hipStream_t)stream));
 }
 

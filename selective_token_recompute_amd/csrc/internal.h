@@ -16,8 +16,10 @@ enum Epi {
 };
 
 // ---- compaction -------------------------------------------------------------
-hipError_t launch_compact(const uint64_t* bits, int B, int N, int32_t* row_seq, int32_t* row_pos,
-                          int32_t* m_b, int32_t* row_start, int32_t* ctl, hipStream_t s);
+// frozen (nullable): positions also out of the active set
+hipError_t launch_compact(const uint64_t* bits, const uint64_t* frozen, int B, int N,
+                          int32_t* row_seq, int32_t* row_pos, int32_t* m_b, int32_t* row_start,
+                          int32_t* ctl, hipStream_t s);
 
 // ---- norms / embedding / rotary ----------------------------------------------
 hipError_t launch_embed_rmsnorm(int dtype, int M, int d, int N, float eps, int mask_id,
@@ -137,7 +139,16 @@ struct LockArgs {
   int32_t* tokens;
   uint64_t* bits;
   int32_t* counters;
+  // SlowFast sampler (sampler 1): exploratory window, k, stage limits and
+  // thresholds; per-sequence frozen bits [B][ceil(N/64)], previous-posterior
+  // flags [B][N] and cycle state [B][kSfStateInts]
+  int sampler, sf_window, sf_k, sf_kmax, sf_whist;
+  float sf_tau_conv, sf_tau_high, sf_var;
+  uint64_t* frozen;
+  int32_t* has_prev;
+  int32_t* sf_state;
 };
+constexpr int kSfStateInts = 16;  // phase, lo, hi, slow_n, hist_n, hist[8], 3 unused
 hipError_t launch_commit_lock(const LockArgs& a, hipStream_t s);
 hipError_t launch_apply_override(int B, int N, int n_commit, const int32_t* cseq,
                                  const int32_t* cpos, const int32_t* ctok, const uint64_t* bits_or,
@@ -145,6 +156,7 @@ hipError_t launch_apply_override(int B, int N, int n_commit, const int32_t* cseq
                                  int32_t* cnt, hipStream_t s);
 hipError_t launch_init_state(int B, int N, int P, int mask_id, const int32_t* prompts,
                              int32_t* tokens, uint64_t* bits, int32_t* counters,
-                             int32_t* has_prev, int32_t* ctl, hipStream_t s);
+                             int32_t* has_prev, int32_t* ctl, uint64_t* frozen,
+                             int32_t* sf_state, hipStream_t s);
 
 }  // namespace dlm

@@ -33,12 +33,20 @@ def model_desc(shape) -> L.dlm_model_desc:
                             L.DLM_BF16 if shape.bf16 else L.DLM_FP32)
 
 
+# SlowFast sampler settings when the lock dict names none ([SF] §4 ablation:
+# at most 8 exploratory steps, history window 2, variance threshold 1.0)
+SF_DEFAULTS = dict(sf_k=1, sf_kmax=8, sf_whist=2, sf_tau_conv=0.9, sf_tau_high=0.9, sf_var=1.0)
+
+
 def run_desc(run, lock: Dict) -> L.dlm_run_desc:
     pol = L.DLM_LOCK_TEST if lock["policy"] == "test" else L.DLM_LOCK_NONE
+    smp = L.DLM_SAMPLER_SLOWFAST if lock.get("sampler") == "slowfast" else L.DLM_SAMPLER_SEMI_AR
+    sf = {k: lock.get(k, v) for k, v in SF_DEFAULTS.items()}
     return L.dlm_run_desc(run.batch, run.seq_len, run.prompt_len, run.steps, run.block_len,
                           float(lock["kl_eps"]), float(lock["conf_tau"]), int(lock["n_consec"]),
                           int(lock.get("kl_dir", 0)), int(lock["lock_prompt_after_first_step"]),
-                          pol)
+                          pol, smp, int(sf["sf_k"]), int(sf["sf_kmax"]), int(sf["sf_whist"]),
+                          float(sf["sf_tau_conv"]), float(sf["sf_tau_high"]), float(sf["sf_var"]))
 
 
 # ---- the C ABI under its own names ---------------------------------------------
@@ -220,6 +228,16 @@ class Engine:
 
     def counters(self) -> torch.Tensor:
         return self._view(L.DLM_GET_COUNTERS, torch.int32, (self.run.batch, self.run.seq_len))
+
+    def frozen_bits(self) -> torch.Tensor:
+        return self._view(L.DLM_GET_FROZEN, torch.int64,
+                          (self.run.batch, (self.run.seq_len + 63) // 64))
+
+    def sf_state(self) -> torch.Tensor:
+        return self._view(L.DLM_GET_SF_STATE, torch.int32, (self.run.batch, L.SF_STATE_INTS))
+
+    def has_prev(self) -> torch.Tensor:
+        return self._view(L.DLM_GET_HAS_PREV, torch.int32, (self.run.batch, self.run.seq_len))
 
     def rows(self):
         return (self._view(L.DLM_GET_ROW_SEQ, torch.int32),

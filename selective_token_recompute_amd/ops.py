@@ -231,3 +231,17 @@ def commit_lock(*, batch, seq_len, prompt_len, mask_id, blk_lo, blk_hi, k, do_co
                                        _p(row_start), _p(row_real), _p(argmax), _p(conf), _p(kl),
                                        _p(has_kl), _p(tokens), _p(bits), _p(counters), _s()),
             "dlm_op_commit_lock")
+
+
+def slowfast_commit(*, batch, seq_len, mask_id, window, sf_k, sf_kmax, sf_whist, sf_tau_conv,
+                    sf_tau_high, sf_var, row_pos, row_start, argmax, conf, tokens, frozen,
+                    has_prev, sf_state):
+    """One SlowFast commit decision per sequence on device arrays; tokens,
+    frozen (int64 view of the uint64 bits), has_prev and sf_state are
+    updated in place."""
+    L.check(L.lib().dlm_op_slowfast_commit(batch, seq_len, mask_id, window, sf_k, sf_kmax,
+                                           sf_whist, float(sf_tau_conv), float(sf_tau_high),
+                                           float(sf_var), _p(row_pos), _p(row_start),
+                                           _p(argmax), _p(conf), _p(tokens), _p(frozen),
+                                           _p(has_prev), _p(sf_state), _s()),
+            "dlm_op_slowfast_commit")

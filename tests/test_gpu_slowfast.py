@@ -1,0 +1,292 @@
+"""SlowFast sampler (SlowFast page, §2 two-stage pipeline) on the GPU.
+
+* The commit op against the oracle's rule on seeded synthetic per-step
+  statistics (several sequences, ties, every stage transition), bit for bit.
+* The engine in lockstep with the oracle (its own forward pass and rule) at
+  a small fp32 width and a bf16 width with two sequences, with a setting
+  that freezes positions and brings them back: active rows (frozen positions
+  absent), logits, statistics (no KL for a position back from frozen), then
+  tokens, locks, frozen set, cycle state and previous-posterior flags bit
+  for bit, the oracle's decision replayed only where it sits within the
+  step's confidence difference of a tie or threshold.
+* The bench's slowfast setting at the full LLaDA-8B shape: invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from selective_token_recompute_amd import _lib as L
+from selective_token_recompute_amd import engine as E
+from selective_token_recompute_amd import ops
+from tests.harness import bits_to_bool, logit_tol
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _f32(x):
+    """A threshold both sides compare against identically (float32 value)."""
+    return float(np.float32(x))
+
+
+def _lock(**kw):
+    d = dict(synth.LOCK_SETTINGS["slowfast"])
+    d.update(kw)
+    for k in ("sf_tau_conv", "sf_tau_high", "sf_var"):
+        d[k] = _f32(d[k])
+    return d
+
+
+def synth_bits(a):
+    B, N = a.shape
+    W = (N + 63) // 64
+    out = np.zeros((B, W), np.uint64)
+    for b in range(B):
+        for i in np.nonzero(a[b])[0]:
+            out[b, i // 64] |= np.uint64(1) << np.uint64(i % 64)
+    return out
+
+
+# --- the commit op on synthetic statistics ---------------------------------------
+
+@pytest.mark.parametrize("seed,k,whist,kmax", [(0, 1, 2, 8), (1, 2, 3, 4), (2, 3, 1, 6),
+                                                (3, 1, 4, 2)])
+def test_slowfast_op_matches_oracle_rule(seed, k, whist, kmax):
+    rng = np.random.default_rng(seed)
+    B, N, P, window, mask = 3, 96, 8, 16, 999
+    lock = _lock(sf_k=k, sf_whist=whist, sf_kmax=kmax, sf_tau_conv=0.5, sf_tau_high=0.75,
+                 sf_var=2.25)
+    run = synth.RunShape(B, N, P, 64, window)
+    x = np.full((B, N), mask, np.int32)
+    x[:, :P] = rng.integers(0, 100, (B, P))
+    frozen = np.zeros((B, N), np.uint8)
+    hp = np.ones((B, N), np.uint8)
+    st = np.zeros((B, 13), np.int32)
+    d_tok = torch.from_numpy(x.copy()).to(DEV)
+    d_frz = torch.zeros((B, (N + 63) // 64), dtype=torch.int64, device=DEV)
+    d_hp = torch.ones((B, N), dtype=torch.int32, device=DEV)
+    d_st = torch.zeros((B, L.SF_STATE_INTS), dtype=torch.int32, device=DEV)
+    transitions = 0
+    for step in range(96):
+        if (x == mask).sum() == 0:
+            break
+        # rows: every position outside the frozen set; confidences (i/32)^4,
+        # exact in float32, mostly low, with ties
+        rows = [np.nonzero(frozen[b] == 0)[0].astype(np.int32) for b in range(B)]
+        confs = [(rng.integers(0, 33, len(r)).astype(np.float64) / 32.0) ** 4 for r in rows]
+        args = [(1000 + r * 7 + step) % 5000 for r in rows]
+        row_pos = np.concatenate(rows)
+        row_start = np.cumsum([0] + [len(r) for r in rows]).astype(np.int32)
+        ops.slowfast_commit(batch=B, seq_len=N, mask_id=mask, window=window, sf_k=k,
+                            sf_kmax=kmax, sf_whist=whist, sf_tau_conv=lock["sf_tau_conv"],
+                            sf_tau_high=lock["sf_tau_high"], sf_var=lock["sf_var"],
+                            row_pos=torch.from_numpy(row_pos).to(DEV),
+                            row_start=torch.from_numpy(row_start).to(DEV),
+                            argmax=torch.from_numpy(np.concatenate(args).astype(np.int32)).to(DEV),
+                            conf=torch.from_numpy(np.concatenate(confs).astype(np.float32)).to(DEV),
+                            tokens=d_tok, frozen=d_frz, has_prev=d_hp, sf_state=d_st)
+        for b in range(B):
+            phase0 = st[b, 0]
+            _, x[b], frozen[b], hp[b], st[b] = oracle.unit_slowfast(
+                run, lock, mask, rows[b], args[b], confs[b], x[b], frozen[b], hp[b], st[b])
+            transitions += int(phase0 != st[b, 0])
+        torch.cuda.synchronize()
+        assert np.array_equal(d_tok.cpu().numpy(), x), f"step {step}: tokens"
+        assert np.array_equal(d_frz.cpu().numpy().view(np.uint64), synth_bits(frozen)), \
+            f"step {step}: frozen"
+        assert np.array_equal(d_hp.cpu().numpy().astype(np.uint8), hp), f"step {step}: has_prev"
+        assert np.array_equal(d_st.cpu().numpy()[:, :13], st), f"step {step}: state"
+    assert transitions >= 4, transitions  # both stages and cycle ends were exercised
+    print(f"\n[slowfast op] seed={seed} steps={step + 1} stage changes={transitions}")
+
+
+# --- the engine in lockstep with the oracle ------------------------------------------
+
+def _engineered_lock(W, shape, run, prompts, **kw):
+    """A SlowFast setting whose first step fixes a span that stops short of
+    the sequence end, so that positions freeze and later return: with one end
+    point in the variance window the first exploratory step already ends the
+    stage; tau_conv is set between two neighbouring confidence levels of the
+    masked positions of sequence 0 in the oracle's first step, as low as
+    possible while the farthest position reaching it stays at least 8
+    positions before the end (the lowest level when every masked row has the
+    same confidence); tau_high = 1 is never reached, so the accelerated stage
+    commits sf_k per step."""
+    orc = oracle.Oracle(shape, W, run, _lock(), prompts)
+    orc.step()
+    rs, rp, _ = orc.rows()
+    conf = orc.stats()["conf"]
+    sel = (rs == 0) & (orc.tokens()[rs, rp] == shape.mask_id)
+    pos, cf = rp[sel], conf[sel]
+    levels = np.unique(cf)[::-1]  # descending
+    best = None
+    for hi_v, lo_v in zip(levels[:-1], levels[1:]):
+        far = int(pos[cf >= hi_v].max())
+        tau = float(np.float32(0.5 * (hi_v + lo_v)))
+        if far > pos.min() and far <= run.seq_len - 9 and lo_v < tau <= hi_v:
+            best = (far, tau)
+    if best is None:
+        best = (int(pos.max()), float(np.float32(levels[-1])))
+    return _lock(sf_whist=1, sf_tau_conv=best[1], sf_tau_high=1.0, **kw), best[0]
+
+
+def _sf_margin(orc, lock, shape, so):
+    """Smallest distance, over this step's masked rows, between confidences
+    of one sequence or between a confidence and a SlowFast threshold: the
+    margin of the step's commit decisions."""
+    rs, rp, _ = orc.rows()
+    masked = orc.tokens()[rs, rp] == shape.mask_id
+    m = np.inf
+    for b in np.unique(rs[masked]):
+        c = np.sort(so["conf"][masked & (rs == b)])
+        if len(c) > 1:
+            m = min(m, float(np.diff(c).min()))
+        m = min(m, float(np.abs(c - lock["sf_tau_conv"]).min()),
+                float(np.abs(c - lock["sf_tau_high"]).min()))
+    return m
+
+
+def run_slowfast_lockstep(shape, W, run, lock, prompts):
+    """Every step on both sides from the same state: active rows (the frozen
+    positions absent), logits and statistics within tolerance; then the
+    commit decision, frozen set, cycle state and previous-posterior flags bit
+    for bit, except where the oracle's own decision sits within twice the
+    step's confidence difference of a tie or a threshold: there the oracle's
+    decision is written into the engine's state and counted."""
+    dw = E.upload_weights(W, shape, DEV)
+    pr = torch.from_numpy(prompts).to(DEV)
+    eng = E.Engine(shape, dw, run, lock, pr)
+    orc = oracle.Oracle(shape, W, run, lock, prompts)
+    B, N = run.batch, run.seq_len
+    rep = dict(steps=0, replays=0, frozen_steps=0, max_frozen=0, returns=0, cycles=0)
+    returned = np.zeros((B, N), bool)  # unfrozen by the last update
+    for t in range(run.steps):
+        m = eng.step()
+        orc.step()
+        torch.cuda.synchronize()
+        seq_o, pos_o, _ = orc.rows()
+        rs, rp, _ = (a.cpu().numpy() for a in eng.rows())
+        assert m == orc.m and np.array_equal(rs, seq_o) and np.array_equal(rp, pos_o), \
+            f"step {t}: active rows"
+        frz = orc.frozen()
+        assert not frz[seq_o, pos_o].any(), f"step {t}: a frozen position is active"
+        if m == 0:
+            orc.lock_update()
+            eng.lock_update()
+            continue
+        _, zo = orc.logits()
+        zg = eng.logits().cpu().numpy()[rs, rp]
+        fin = np.isfinite(zo)
+        assert np.array_equal(fin, np.isfinite(zg)), f"step {t}: -inf pattern"
+        with np.errstate(invalid="ignore"):
+            dz = np.abs(np.where(fin, zg - zo, 0.0))
+        scale = float(np.abs(zo[fin]).max())
+        assert dz.max() <= logit_tol(shape, scale), f"step {t}: logits {dz.max():.3g}"
+        so = orc.stats()
+        sg = {k: v.cpu().numpy() for k, v in eng.stats().items()}
+        assert np.array_equal(sg["has_kl"].astype(np.uint8), so["has_kl"]), f"step {t}: has_kl"
+        back = returned[seq_o, pos_o]
+        assert not so["has_kl"][back].any(), f"step {t}: KL on a position back from frozen"
+        rep["returns"] += int(back.sum())
+        dconf = float(np.abs(sg["conf"] - so["conf"]).max())
+        margin = _sf_margin(orc, lock, shape, so)
+        st0 = orc.sf_state()[:, 0].copy()
+        frozen_before = orc.frozen().astype(bool)
+        orc.lock_update()
+        eng.lock_update()
+        torch.cuda.synchronize()
+        want = dict(tokens=orc.tokens(), locks=orc.locked(), frozen=orc.frozen(),
+                    state=orc.sf_state(), has_prev=orc.has_prev())
+        got = dict(tokens=eng.tokens().cpu().numpy(),
+                   locks=bits_to_bool(eng.lock_bits().cpu().numpy().view(np.uint64), N),
+                   frozen=bits_to_bool(eng.frozen_bits().cpu().numpy().view(np.uint64), N),
+                   state=eng.sf_state().cpu().numpy()[:, :13],
+                   has_prev=eng.has_prev().cpu().numpy().astype(np.uint8))
+        diff = [k for k in want if not np.array_equal(got[k], want[k].reshape(got[k].shape))]
+        if diff:
+            assert margin <= 2.0 * dconf + 1e-12, \
+                f"step {t}: {diff} differ with decision margin {margin:.3g} > 2 x {dconf:.3g}"
+            eng.tokens().copy_(torch.from_numpy(want["tokens"]).to(DEV))
+            eng.lock_bits().copy_(torch.from_numpy(
+                synth_bits(want["locks"]).view(np.int64)).to(DEV))
+            eng.counters().copy_(torch.from_numpy(orc.counters()).to(DEV))
+            eng.frozen_bits().copy_(torch.from_numpy(
+                synth_bits(want["frozen"]).view(np.int64)).to(DEV))
+            sf = eng.sf_state()
+            sf[:, :13].copy_(torch.from_numpy(want["state"]).to(DEV))
+            eng.has_prev().copy_(torch.from_numpy(want["has_prev"].astype(np.int32)).to(DEV))
+            torch.cuda.synchronize()
+            rep["replays"] += 1
+        rep["steps"] += 1
+        rep["cycles"] += int(((st0 == 1) & (want["state"][:, 0] == 0)).sum())
+        rep["frozen_steps"] += int(want["frozen"].any())
+        rep["max_frozen"] = max(rep["max_frozen"], int(want["frozen"].sum()))
+        returned = frozen_before & ~want["frozen"].astype(bool)
+    eng.close()
+    return rep
+
+
+TINY_SF_RUN = synth.RunShape(2, 64, 8, 32, 8)
+
+
+@pytest.fixture(scope="module")
+def tiny_case():
+    shape, _ = synth.CONFIGS["tiny"]
+    return shape, synth.gen_weights(shape), synth.gen_prompts(shape, TINY_SF_RUN)
+
+
+def test_slowfast_lockstep_tiny_fp32(tiny_case):
+    shape, W, pr = tiny_case
+    lock, e = _engineered_lock(W, shape, TINY_SF_RUN, pr, sf_k=2, sf_kmax=4)
+    rep = run_slowfast_lockstep(shape, W, TINY_SF_RUN, lock, pr)
+    print(f"\n[slowfast tiny fp32] end point {e} {rep}")
+    assert rep["frozen_steps"] > 0 and rep["returns"] > 0 and rep["cycles"] > 0
+    assert rep["replays"] <= rep["steps"] // 4
+
+
+def test_slowfast_lockstep_bf16_two_sequences():
+    shape = synth.ModelShape(2, 512, 4, 4, 128, 1024, 4096, bf16=True)
+    run = synth.RunShape(2, 192, 64, 48, 32)
+    W = synth.gen_weights(shape)
+    pr = synth.gen_prompts(shape, run)
+    lock, e = _engineered_lock(W, shape, run, pr, sf_k=3, sf_kmax=6)
+    rep = run_slowfast_lockstep(shape, W, run, lock, pr)
+    print(f"\n[slowfast bf16] end point {e} {rep}")
+    assert rep["cycles"] > 0
+
+
+def test_slowfast_llada_full_shape_invariants():
+    """The bench's slowfast setting at the full LLaDA-8B shape: decoded and
+    locked tokens never change, the frozen set holds only masked positions
+    beyond the span and is absent from the active set, each step commits at
+    least one position while masks remain (random weights: no confidence
+    reaches 0.9, so every cycle ends by sf_kmax)."""
+    shape, run = synth.CONFIGS["llada8b"]
+    dw = E.random_device_weights(shape, seed=0)
+    pr = torch.from_numpy(synth.gen_prompts(shape, run)).to(DEV)
+    lock = _lock()
+    eng = E.Engine(shape, dw, run, lock, pr)
+    N = run.seq_len
+    prev = eng.tokens().cpu().numpy().copy()
+    prev_lk = np.zeros((1, N), np.uint8)
+    for t in range(24):
+        eng.step()
+        rs, rp, _ = (a.cpu().numpy() for a in eng.rows())
+        frz = bits_to_bool(eng.frozen_bits().cpu().numpy().view(np.uint64), N).astype(bool)
+        assert not frz[rs, rp].any()
+        eng.lock_update()
+        tok = eng.tokens().cpu().numpy()
+        lk = bits_to_bool(eng.lock_bits().cpu().numpy().view(np.uint64), N)
+        frz = bits_to_bool(eng.frozen_bits().cpu().numpy().view(np.uint64), N).astype(bool)
+        st = eng.sf_state().cpu().numpy()[0]
+        dec = prev != shape.mask_id
+        assert np.array_equal(tok[dec], prev[dec]) and (lk >= prev_lk).all()
+        if (prev == shape.mask_id).any():
+            assert (tok != prev).sum() >= 1, f"step {t}: no progress"
+        assert (tok[frz] == shape.mask_id).all()
+        if frz.any():
+            assert st[0] == 1 and np.nonzero(frz[0])[0].min() >= st[2]
+        prev, prev_lk = tok.copy(), lk
+    eng.close()
