@@ -74,6 +74,30 @@ def test_invalid_run_rejected(field, value):
     assert E.dlm_state_bytes(m, r) == 0
 
 
+@pytest.mark.parametrize("field,value", [
+    ("sampler", 2), ("sf_k", 0), ("sf_kmax", 0), ("sf_whist", 0), ("sf_whist", 9),
+    ("sf_tau_conv", float("nan")), ("sf_tau_high", float("nan")), ("sf_var", float("nan"))])
+def test_invalid_slowfast_run_rejected(field, value):
+    shape, run = synth.CONFIGS["llada8b"]
+    m, r = E.model_desc(shape), E.run_desc(run, synth.LOCK_SETTINGS["slowfast"])
+    assert E.dlm_state_bytes(m, r) > 0
+    setattr(r, field, value)
+    assert E.dlm_state_bytes(m, r) == 0
+
+
+def test_slowfast_sequence_limit():
+    # the commit kernel stages a sequence's candidates in LDS: seq_len <= 4096
+    import dataclasses
+    shape, run = synth.CONFIGS["longctx"]
+    lock = synth.LOCK_SETTINGS["slowfast"]
+    assert E.dlm_state_bytes(E.model_desc(shape), E.run_desc(run, lock)) > 0
+    big = dataclasses.replace(run, seq_len=4160)
+    assert E.dlm_state_bytes(E.model_desc(shape), E.run_desc(big, lock)) == 0
+    # the semi-autoregressive sampler has no such limit
+    assert E.dlm_state_bytes(E.model_desc(shape),
+                             E.run_desc(big, synth.LOCK_SETTINGS["natural"])) > 0
+
+
 def test_steps_fewer_than_blocks_rejected():
     shape, run = synth.CONFIGS["longctx"]
     import dataclasses
@@ -120,6 +144,15 @@ def test_op_argument_validation():
     assert lib.dlm_op_compact(None, 1, 8, None, None, None, None, None, None) == L.DLM_E_INVALID
     assert lib.dlm_op_commit_lock(1, 8, 2, 15, 6, 2, 1, 1, 1, 1, 0.0, 0.0, 1, 0,
                                   *([None] * 11), None) == L.DLM_E_INVALID
+    # slowfast_commit: null arrays, then bad sizes with (dummy) non-null arrays
+    assert lib.dlm_op_slowfast_commit(1, 8, 7, 4, 1, 8, 2, 0.5, 0.9, 1.0,
+                                      *([None] * 8), None) == L.DLM_E_INVALID
+    buf = (ctypes.c_uint8 * 64)()
+    p = ctypes.addressof(buf)
+    for args in [(1, 5000, 7, 4, 1, 8, 2), (1, 8, 7, 0, 1, 8, 2), (1, 8, 7, 4, 0, 8, 2),
+                 (1, 8, 7, 4, 1, 8, 9), (0, 8, 7, 4, 1, 8, 2)]:
+        assert lib.dlm_op_slowfast_commit(*args, 0.5, 0.9, 1.0, *([p] * 8),
+                                          None) == L.DLM_E_INVALID
 
 
 def test_workspace_queries():
