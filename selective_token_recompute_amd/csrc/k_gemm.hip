@@ -445,13 +445,16 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void gemm_bf16_mfma_kernel(
             }
           }
         } else {
-          // V head, stored transposed: item = (row quad, chunk column w)
+          // V head, stored transposed: item = (row quad, chunk column w),
+          // row quads fastest so that a wave's stores go to consecutive
+          // positions of one V^T row (one head-dimension column)
           const int gv = hix - nq - nkv;
-          constexpr int ITEMS = (PR / 4) * 64, ITER = (ITEMS + NT - 1) / NT;
+          constexpr int QN = PR / 4;  // row quads per pass
+          constexpr int ITEMS = QN * 64, ITER = (ITEMS + NT - 1) / NT;
 #pragma unroll
           for (int k = 0; k < ITER; ++k) {
             const int it = tid + k * NT;
-            const int w = it & 63, r4 = (it >> 6) * 4;
+            const int w = it / QN, r4 = (it - w * QN) * 4;
             const int c = (w & 32) * 2 + hb * 32 + (w & 31);  // head dimension
             const int row = r0 + r4;
             if (it < ITEMS && row < M) {
