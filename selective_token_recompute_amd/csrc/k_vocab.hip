@@ -141,7 +141,18 @@ __global__ __launch_bounds__(256) void vocab_merge_parts_kernel(
   if (r >= M) return;  // wave-uniform
   VPart t = vpart_empty();
   const VPart* p = part + (size_t)r * nparts;
-  for (int c = lane; c < nparts; c += 64) t = vmerge(t, p[c]);
+  // four partials loaded before any is merged, so that a lane's loads are in
+  // flight together (the merges form one dependent chain)
+  constexpr int U = 4;
+  int c = lane;
+  for (; c + (U - 1) * 64 < nparts; c += U * 64) {
+    VPart q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) q[u] = p[c + u * 64];
+#pragma unroll
+    for (int u = 0; u < U; ++u) t = vmerge(t, q[u]);
+  }
+  for (; c < nparts; c += 64) t = vmerge(t, p[c]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) t = vmerge(t, vpart_shfl_xor(t, o));
   if (lane == 0)
