@@ -12,6 +12,7 @@ import oracle
 import synth
 from selective_token_recompute_amd import _lib as L
 from selective_token_recompute_amd import ops
+from tests.harness import top2_gap
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -286,7 +287,7 @@ LMSTATS_CFGS = [1, 5, 6, 7, 8, 9, 10, 12, 13, 14, 24, 25, 28]  # tiles the fused
 def _lm_head_stats_case(M, V, K, kl_dir, cfg=-1, seed=0, A=None, W=None):
     """Runs the fused LM head on M rows scattered over B=2 sequences of 96
     positions; returns (GPU outputs, the GPU's stored logits of the rows, the
-    oracle's logits, the oracle's statistics of the GPU's logits, context)."""
+    oracle's logits, the oracle's statistics of its own logits, context)."""
     B, N = 2, 96
     rng = np.random.default_rng(seed)
     flat = np.sort(rng.choice(B * N, M, replace=False))
@@ -311,7 +312,9 @@ def _lm_head_stats_case(M, V, K, kl_dir, cfg=-1, seed=0, A=None, W=None):
     z = Z.cpu().numpy()
     got = z[rs, rp]
     prev_logp = zprev[rs, rp].astype(np.float64) - lse_prev[rs, rp].astype(np.float64)[:, None]
-    ref = oracle.unit_vocab_stats(got, prev_logp, hp[rs, rp].astype(np.uint8), mask_id=V - 1,
+    zo = zref.copy()
+    zo[:, V - 1] = -np.inf
+    ref = oracle.unit_vocab_stats(zo, prev_logp, hp[rs, rp].astype(np.uint8), mask_id=V - 1,
                                   kl_dir=kl_dir)
     ctx = dict(rs=rs, rp=rp, z=z, hp=hp, hp_after=hp_d.cpu().numpy(),
                lse_cur=lse_cur.cpu().numpy(), zprev=zprev, lse_prev=lse_prev)
@@ -326,21 +329,28 @@ def _check_lm_head_stats(g, got, zref, ref, ctx, V):
     untouched = np.ones(ctx["z"].shape[:2], bool)
     untouched[rs, rp] = False
     assert (ctx["z"][untouched] == 7.0).all()
-    # the statistics of those logits
+    # the statistics against the oracle's statistics of its own (fp64) logits:
+    # with every logit within dz of the oracle's, lse moves by at most dz, the
+    # confidence by a factor within e^(+-2 dz), KL by at most 4 dz (plus fp32
+    # accumulation); argmax may differ only where the oracle's top two logits
+    # are within 2 dz
+    dz = float(np.abs(got[:, :-1] - zref[:, :-1]).max())
     hk = ctx["hp"][rs, rp].astype(bool)
-    assert np.array_equal(g["argmax"], ref["argmax"])
-    assert np.allclose(g["conf"], ref["conf"], rtol=1e-5, atol=0)
-    assert np.allclose(g["lse"], ref["lse"], rtol=0, atol=2e-5)
+    gap = top2_gap(zref, V - 1)
+    bad = g["argmax"] != ref["argmax"]
+    assert not (bad & (gap > 2.0 * dz + 1e-12)).any(), (int(bad.sum()), dz)
+    assert (np.abs(g["conf"] - ref["conf"]) <= ref["conf"] * (2.5 * dz + 1e-5) + 1e-7).all()
+    assert (np.abs(g["lse"] - ref["lse"]) <= dz + 2e-5).all()
     assert np.array_equal(g["has_kl"].astype(bool), hk)
     assert np.isnan(g["kl"][~hk]).all()
     if hk.any():
-        assert np.allclose(g["kl"][hk], ref["kl"][hk], rtol=1e-3, atol=2e-6), \
-            np.abs(g["kl"][hk] - ref["kl"][hk]).max()
+        err = np.abs(g["kl"][hk] - ref["kl"][hk])
+        assert (err <= 1e-3 * np.abs(ref["kl"][hk]) + 4.0 * dz + 2e-6).all(), err.max()
     # per-position state: has_prev set and lse recorded at the active slots only
     after = ctx["hp"].copy()
     after[rs, rp] = 1
     assert np.array_equal(ctx["hp_after"], after)
-    assert np.allclose(ctx["lse_cur"][rs, rp], ref["lse"], atol=2e-5)
+    assert (np.abs(ctx["lse_cur"][rs, rp] - ref["lse"]) <= dz + 2e-5).all()
     assert (ctx["lse_cur"][untouched] == -5.0).all()
     assert g["err"][0] == 0
 
