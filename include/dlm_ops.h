@@ -115,7 +115,11 @@ int dlm_op_attention(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, i
  * the default plan), LDS ring depth (stages 2 or 4; 0: the plan's), number
  * of key groups (key_halves 1, 2 or 4: waves sharing each block of 16
  * queries, each over its share of every key tile, merged by log-sum-exp; 0:
- * the plan's) and 16-query blocks per wave (qblocks 1 or 2; 0: the plan's),
+ * the plan's), 16-query blocks per wave (qblocks 1 or 2; 0: the plan's) and
+ * keys per LDS tile (key_tile 64 or 128; 0: the plan's, which takes 128
+ * only together with four key groups of its own choosing; a tile that does
+ * not divide seq_len falls back to 64; 128-key tiles always run a 2-stage
+ * ring),
  * for tuning sweeps; the layouts built are (key groups, query blocks) =
  * (1, 1), (2, 1), (4, 1), (2, 2), (4, 2), any other pair runs (2, 1).  ws
  * must hold dlm_op_attention_config_ws_bytes() bytes; DLM_E_SIZE otherwise. */
@@ -124,8 +128,8 @@ size_t dlm_op_attention_config_ws_bytes(int32_t dtype, int32_t M, int32_t batch,
 int dlm_op_attention_config(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, int32_t nq,
                             int32_t nkv, int32_t hd, const void* q, const int32_t* row_start,
                             const void* kcache, const void* vcache, void* o, int32_t splits,
-                            int32_t stages, int32_t key_halves, int32_t qblocks, void* ws,
-                            size_t ws_bytes, void* stream);
+                            int32_t stages, int32_t key_halves, int32_t qblocks,
+                            int32_t key_tile, void* ws, size_t ws_bytes, void* stream);
 
 /* QKV projection with the rotary embedding and the K/V cache scatter in the
  * GEMM epilogue (SureLock page, §2: fresh Q/K/V only for the active rows,

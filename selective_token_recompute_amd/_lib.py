@@ -123,7 +123,7 @@ def lib() -> ctypes.CDLL:
         L.dlm_op_attention.argtypes = [i32] * 7 + [vp] * 5 + [vp, sz, vp]
         L.dlm_op_attention_config_ws_bytes.restype = sz
         L.dlm_op_attention_config_ws_bytes.argtypes = [i32] * 8
-        L.dlm_op_attention_config.argtypes = [i32] * 7 + [vp] * 5 + [i32] * 4 + [vp, sz, vp]
+        L.dlm_op_attention_config.argtypes = [i32] * 7 + [vp] * 5 + [i32] * 5 + [vp, sz, vp]
         L.dlm_op_vocab_ws_bytes.restype = sz
         L.dlm_op_vocab_ws_bytes.argtypes = [i32, i32]
         L.dlm_op_vocab_stats.argtypes = [i32, i32, i32, i32, i32] + [vp] * 14 + [sz, vp]

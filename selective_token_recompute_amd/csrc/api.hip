@@ -788,12 +788,12 @@ size_t dlm_op_attention_config_ws_bytes(int32_t dtype, int32_t M, int32_t batch,
 int dlm_op_attention_config(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, int32_t nq,
                             int32_t nkv, int32_t hd, const void* q, const int32_t* row_start,
                             const void* kcache, const void* vcache, void* o, int32_t splits,
-                            int32_t stages, int32_t key_halves, int32_t qblocks, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            int32_t stages, int32_t key_halves, int32_t qblocks,
+                            int32_t key_tile, void* ws, size_t ws_bytes, void* stream) {
   if (!dt_ok(dtype) || M < 0 || batch < 1 || seq_len < 1 || nq < 1 || nkv < 1 || nq % nkv ||
       hd < 2 || hd > 256 || (hd & 1) || splits < 0 || (stages != 0 && stages != 2 && stages != 4) ||
       (key_halves != 0 && key_halves != 1 && key_halves != 2 && key_halves != 4) ||
-      qblocks < 0 || qblocks > 2)
+      qblocks < 0 || qblocks > 2 || (key_tile != 0 && key_tile != 64 && key_tile != 128))
     return DLM_E_INVALID;
   if (M == 0) return DLM_OK;
   if (!q || !row_start || !kcache || !vcache || !o) return DLM_E_INVALID;
@@ -801,7 +801,7 @@ int dlm_op_attention_config(int32_t dtype, int32_t M, int32_t batch, int32_t seq
     return DLM_E_SIZE;
   return hip_status(launch_attention_cfg(dtype, M, batch, seq_len, nq, nkv, hd, q, row_start,
                                          kcache, vcache, o, ws, ws ? ws_bytes : 0, splits, stages,
-                                         key_halves, qblocks, (hipStream_t)stream));
+                                         key_halves, qblocks, key_tile, (hipStream_t)stream));
 }
 
 size_t dlm_op_vocab_ws_bytes(int32_t M, int32_t V) {

@@ -109,7 +109,8 @@ size_t attention_cfg_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, i
 hipError_t launch_attention_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd,
                                 const void* q, const int32_t* row_start, const void* kc,
                                 const void* vc, void* o, void* ws, size_t ws_bytes, int splits,
-                                int stages, int key_halves, int qblocks, hipStream_t s);
+                                int stages, int key_halves, int qblocks, int key_tile,
+                                hipStream_t s);
 
 // ---- vocabulary statistics ----------------------------------------------------------
 size_t vocab_ws_bytes(int M, int V);

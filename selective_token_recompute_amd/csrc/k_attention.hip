@@ -195,12 +195,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   }
 }
 
-// DMA variant (N % 64 == 0): K and V^T tiles go straight from global memory
-// into a STAGES-deep LDS ring with global_load_lds_dwordx4, the next tiles in
-// flight while the current one is consumed.  K tile rows (one key, HD
-// elements) and V^T tile rows (one hd column, 64 keys = 128 B) are stored with
-// their 16-byte chunks XOR-swizzled by the row index so that the fragment
-// reads hit distinct banks.
+// DMA variant (N a multiple of the key tile KT = 64 or 128): K and V^T tiles
+// go straight from global memory into a STAGES-deep LDS ring with
+// global_load_lds_dwordx4, the next tiles in flight while the current one is
+// consumed.  K tile rows (one key, HD elements) and V^T tile rows (one hd
+// column, KT keys = 128 or 256 B) are stored with their 16-byte chunks
+// XOR-swizzled by the row index so that the fragment reads hit distinct
+// banks.
 typedef __attribute__((address_space(3))) void attn_lds_void;
 __device__ __forceinline__ void attn_dma16(const void* g, unsigned char* lds) {
   __builtin_amdgcn_global_load_lds(g, (attn_lds_void*)lds, 16, 0, 0);
@@ -213,6 +214,9 @@ __device__ __forceinline__ void attn_dma16(const void* g, unsigned char* lds) {
 // share banks; that pairing, not the XOR, leaves two-way conflicts there.)
 __device__ __forceinline__ int kswz(int r, int chunks) { return chunks == 16 ? (r & 15) : (r & 7); }
 __device__ __forceinline__ int vswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// 256-byte V^T rows (128-key tiles): the 16 rows a fragment read touches get
+// 16 distinct 16-byte slots of one chunk
+__device__ __forceinline__ int vswz16(int r) { return r & 15; }
 // Reductions over the lanes l, l^16, l^32, l^48 with the gfx950 lane-swap
 // instructions: permlane16_swap(v, v) returns v from lanes l and l^16 in its
 // two outputs, permlane32_swap(v, v) from lanes l and l^32.
@@ -274,7 +278,7 @@ constexpr size_t attn_merge_bytes() {
                  : (size_t)(KH / 2) * (4 / QB) * (QB * (HD / 16) * 64 * 16 + QB * 64 * 8);
 }
 
-template <int HD, bool SPLIT, int STAGES, int KH, int QB>
+template <int HD, bool SPLIT, int STAGES, int KH, int QB, int KT>
 __global__ __launch_bounds__(64 * (4 / QB) * KH) void attn_mfma_dma_kernel(
     const bf16_t* __restrict__ q, const int32_t* __restrict__ row_start,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ o, int N,
@@ -282,12 +286,14 @@ __global__ __launch_bounds__(64 * (4 / QB) * KH) void attn_mfma_dma_kernel(
     float* __restrict__ part_ml) {
   static_assert(KH == 1 || KH == 2 || KH == 4, "key groups");
   static_assert(QB == 1 || QB == 2, "query blocks per wave");
+  static_assert(KT == 64 || KT == 128, "key tile");
   constexpr int QW = 4 / QB;                        // query waves
   constexpr int NWV = QW * KH;                      // waves
-  constexpr int NKB = 4 / KH;                       // 16-key blocks per wave per tile
+  constexpr int NKB = KT / (16 * KH);               // 16-key blocks per wave per tile
   constexpr int NKC = HD / 32, NCB = HD / 16;
   constexpr int KCH = HD / 8;                       // 16-byte chunks per K row
-  constexpr int K_BYTES = kAttnKeys * HD * 2, V_BYTES = HD * kAttnKeys * 2;
+  constexpr int VRB = KT * 2, VCH = VRB / 16;       // V^T row bytes, 16-byte chunks per row
+  constexpr int K_BYTES = KT * HD * 2, V_BYTES = HD * KT * 2;
   constexpr int STAGE = K_BYTES + V_BYTES;
   constexpr int K_INSTR = K_BYTES / 1024, V_INSTR = V_BYTES / 1024;
   constexpr int IPW = (K_INSTR + V_INSTR) / NWV;    // per wave
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(64 * (4 / QB) * KH) void attn_mfma_dma_kernel(
   const bf16_t* vslab = vc + slab;  // [HD][N]
   const int key0 = bz * keys_per_split;
   const int key1 = min(N, key0 + keys_per_split);
-  const int ntiles = key1 > key0 ? (key1 - key0) / kAttnKeys : 0;
+  const int ntiles = key1 > key0 ? (key1 - key0) / KT : 0;
   const float scale = kLog2e / sqrtf((float)HD);
 
   // this lane's global source for each of its DMA instructions (tile 0)
@@ -344,8 +350,8 @@ __global__ __launch_bounds__(64 * (4 / QB) * KH) void attn_mfma_dma_kernel(
       dst[i] = j * 1024;
     } else {
       const int jv = j - K_INSTR;
-      const int vr = jv * 8 + (lane >> 3);                      // hd row of V^T
-      const int lc = (lane & 7) ^ vswz(vr);
+      const int vr = jv * (1024 / VRB) + lane / VCH;           // hd row of V^T
+      const int lc = (lane % VCH) ^ (VCH == 16 ? vswz16(vr) : vswz(vr));
       src[i] = vslab + (size_t)vr * N + key0 + lc * 8;
       dst[i] = K_BYTES + jv * 1024;
     }
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(64 * (4 / QB) * KH) void attn_mfma_dma_kernel(
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int j = wave + i * NWV;
-      const size_t adv = j < K_INSTR ? (size_t)t * kAttnKeys * HD : (size_t)t * kAttnKeys;
+      const size_t adv = j < K_INSTR ? (size_t)t * KT * HD : (size_t)t * KT;
       attn_dma16(src[i] + adv, st + dst[i]);
     }
   };
@@ -390,7 +396,7 @@ __global__ __launch_bounds__(64 * (4 / QB) * KH) void attn_mfma_dma_kernel(
     }
   }
 
-  const int kofs = kh * (kAttnKeys / KH);  // first key of this wave in a tile
+  const int kofs = kh * (KT / KH);  // first key of this wave in a tile
   for (int t = 0; t < ntiles; ++t) {
     // this wave's loads of tile t (later tiles may stay in flight), then
     // everyone's; every wave is done with tile t-1 after the barrier
@@ -460,8 +466,9 @@ __global__ __launch_bounds__(64 * (4 / QB) * KH) void attn_mfma_dma_kernel(
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int u = (kofs + kb * 16) / 4 + (lane >> 4);  // 8-byte unit: 4 keys
-        const s16x4 va = *(const s16x4*)(st + K_BYTES + vr * 128 +
-                                          (((u >> 1) ^ vswz(vr)) << 4) + ((u & 1) << 3));
+        const int vx = VCH == 16 ? vswz16(vr) : vswz(vr);
+        const s16x4 va = *(const s16x4*)(st + K_BYTES + vr * VRB + (((u >> 1) ^ vx) << 4) +
+                                          ((u & 1) << 3));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           oacc[qb][cb] =
@@ -628,6 +635,7 @@ struct AttnPlan {
   int qtiles, splits, keys_per_split, stages;
   int key_halves;  // key groups: waves per query block, each over its share of every key tile
   int qblocks;     // 16-query blocks per wave
+  int key_tile;    // keys per LDS tile of the DMA kernel (64 or 128)
   size_t ws;
 };
 
@@ -645,8 +653,9 @@ constexpr size_t kAttnSplitCap = 64ull << 20;  // split-KV partials never exceed
 // whether 32 or 192 workgroups run, so the time is per-workgroup latency
 // rather than HBM, LDS or MFMA throughput.
 AttnPlan make_attn_plan_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits_in,
-                            int stages_in, int kh_in, int qb_in) {
+                            int stages_in, int kh_in, int qb_in, int kt_in) {
   AttnPlan p{};
+  p.key_tile = (kt_in == 128 && N % 128 == 0) ? 128 : 64;
   p.key_halves = kh_in == 1 || kh_in == 2 || kh_in == 4 ? kh_in : 2;
   p.qblocks = qb_in == 1 || qb_in == 2 ? qb_in : 1;
   p.mfma = dtype == kBF16 && (hd == 64 || hd == 128) && nq % nkv == 0;
@@ -659,7 +668,7 @@ AttnPlan make_attn_plan_cfg(int dtype, int M, int B, int N, int nq, int nkv, int
   p.qtiles = (mb_max * G + kAttnQ - 1) / kAttnQ;
   // estimated busy workgroups: the rows are spread over the sequences
   const int busy = std::max(1, (M * G + kAttnQ - 1) / kAttnQ) * nkv;
-  const int ktiles = (N + kAttnKeys - 1) / kAttnKeys;
+  const int ktiles = (N + p.key_tile - 1) / p.key_tile;
   auto ws_of = [&](int sp) { return (size_t)sp * M * nq * (hd + 2) * sizeof(float); };
   int splits = 1;
   if (splits_in > 0) {
@@ -670,50 +679,59 @@ AttnPlan make_attn_plan_cfg(int dtype, int M, int B, int N, int nq, int nkv, int
   }
   p.splits = splits;
   const int tiles_per = (ktiles + splits - 1) / splits;
-  p.keys_per_split = tiles_per * kAttnKeys;
-  // four key groups (16 waves) when every workgroup runs at once on its own
-  // CU and walks at least 64 key tiles: 5-6% faster at N = 4096 with 32 or
-  // 192 workgroups, slower at N <= 1024; with many more workgroups than CUs
-  // (N = 4096 over thousands of query tiles) about 30% slower than two
-  if (kh_in == 0 && tiles_per >= 64 && busy * splits <= 256) p.key_halves = 4;
+  p.keys_per_split = tiles_per * p.key_tile;
+  // four key groups (16 waves) with 128-key tiles when every workgroup runs
+  // at once on its own CU and walks at least 1024 keys.  Measured at M = 384,
+  // 32 heads: 4% faster at N = 1024, 12% at N = 2048, 17% at N = 4096 than
+  // two groups of 64-key tiles, 4% slower at N = 512.  The larger tile pays
+  // only with four groups (two groups with 128-key tiles are level with
+  // 64-key tiles): the per-tile cost is mostly fixed (load issue, barrier,
+  // fragment reads).  With many more workgroups than CUs (N = 4096 over
+  // thousands of query tiles) four groups ran about 30% slower than two.
+  if (kh_in == 0 && p.keys_per_split >= 1024 && busy * splits <= 256) {
+    p.key_halves = 4;
+    // a split range of an even number of 64-key tiles is a whole number of
+    // 128-key tiles; keys_per_split is unchanged
+    if (kt_in == 0 && N % 128 == 0 && tiles_per % 2 == 0) p.key_tile = 128;
+  }
   p.stages = stages_in == 2 || stages_in == 4 ? stages_in : 2;
   p.ws = splits > 1 ? ws_of(splits) : 0;
   return p;
 }
 
 AttnPlan make_attn_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd) {
-  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, 0, 0, 0, 0);
+  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, 0, 0, 0, 0, 0);
 }
 
-template <int HD, bool SPLIT, int STAGES, int KH, int QB>
+template <int HD, bool SPLIT, int STAGES, int KH, int QB, int KT>
 void launch_attn_dma(dim3 grid, const void* q, const int32_t* row_start, const void* kc,
                      const void* vc, void* o, int N, int nq, int nkv, int kps, int M, float* po,
                      float* pml, hipStream_t s) {
-  constexpr size_t ring = STAGES * (size_t)(2 * kAttnKeys * HD * 2);
+  constexpr size_t ring = STAGES * (size_t)(2 * KT * HD * 2);
   constexpr size_t merge = attn_merge_bytes<HD, KH, QB>();
   constexpr size_t lds = ring > merge ? ring : merge;
   static_assert(lds <= 160 * 1024, "LDS of a CU");
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH, QB>),
+        reinterpret_cast<const void*>(&attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH, QB, KT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH, QB><<<grid, 64 * (4 / QB) * KH, lds, s>>>(
+  attn_mfma_dma_kernel<HD, SPLIT, STAGES, KH, QB, KT><<<grid, 64 * (4 / QB) * KH, lds, s>>>(
       (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq, nkv,
       kps, M, po, pml);
 }
 
 // Wave layouts built: (key groups, query blocks per wave) = (1, 1), (2, 1),
 // (4, 1), (2, 2), (4, 2); any other request takes (2, 1).
-template <int HD, bool SPLIT, int STAGES>
+template <int HD, bool SPLIT, int STAGES, int KT>
 void launch_attn_dma_layout(int kh, int qb, dim3 grid, const void* q, const int32_t* row_start,
                             const void* kc, const void* vc, void* o, int N, int nq, int nkv,
                             int kps, int M, float* po, float* pml, hipStream_t s) {
-#define DLM_ATTN_LAUNCH(KH, QB)                                                                \
-  launch_attn_dma<HD, SPLIT, STAGES, KH, QB>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, \
-                                             po, pml, s)
+#define DLM_ATTN_LAUNCH(KH, QB)                                                              \
+  launch_attn_dma<HD, SPLIT, STAGES, KH, QB, KT>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, \
+                                                 M, po, pml, s)
   if (qb == 2 && kh == 4) DLM_ATTN_LAUNCH(4, 2);
   else if (qb == 2 && kh == 2) DLM_ATTN_LAUNCH(2, 2);
   else if (kh == 4) DLM_ATTN_LAUNCH(4, 1);
@@ -723,17 +741,21 @@ void launch_attn_dma_layout(int kh, int qb, dim3 grid, const void* q, const int3
 }
 
 template <int HD, bool SPLIT>
-void launch_attn_kernel(dim3 grid, bool dma, int stages, int kh, int qb, const void* q,
+void launch_attn_kernel(dim3 grid, bool dma, int stages, int kh, int qb, int kt, const void* q,
                         const int32_t* row_start,
                         const void* kc, const void* vc, void* o, int N, int nq, int nkv,
                         int kps, int M, float* po, float* pml, hipStream_t s) {
   if (dma) {
-    if (stages == 2)
-      launch_attn_dma_layout<HD, SPLIT, 2>(kh, qb, grid, q, row_start, kc, vc, o, N, nq, nkv, kps,
-                                           M, po, pml, s);
-    else
-      launch_attn_dma_layout<HD, SPLIT, 4>(kh, qb, grid, q, row_start, kc, vc, o, N, nq, nkv, kps,
-                                           M, po, pml, s);
+#define DLM_ATTN_STAGES(ST, KT)                                                              \
+  launch_attn_dma_layout<HD, SPLIT, ST, KT>(kh, qb, grid, q, row_start, kc, vc, o, N, nq, nkv, \
+                                            kps, M, po, pml, s)
+    if (kt == 128) {
+      DLM_ATTN_STAGES(2, 128);  // four 64 KB stages would not fit the LDS at hd 128
+    } else {
+      if (stages == 2) DLM_ATTN_STAGES(2, 64);
+      else DLM_ATTN_STAGES(4, 64);
+    }
+#undef DLM_ATTN_STAGES
   } else {
     attn_mfma_kernel<HD, SPLIT><<<grid, 256, 0, s>>>((const bf16_t*)q, row_start,
                                                      (const bf16_t*)kc, (const bf16_t*)vc,
@@ -746,20 +768,22 @@ hipError_t run_attn_mfma(const AttnPlan& p, int M, int B, int N, int nq, int nkv
                          const void* q, const int32_t* row_start, const void* kc,
                          const void* vc, void* o, void* ws, hipStream_t s) {
   dim3 grid(p.qtiles, B * nkv, p.splits);
-  const bool dma = (N % kAttnKeys) == 0;
+  const bool dma = (N % p.key_tile) == 0;
   if (p.splits > 1) {
     float* po = (float*)ws;
     float* pml = po + (size_t)p.splits * M * nq * HD;
-    launch_attn_kernel<HD, true>(grid, dma, p.stages, p.key_halves, p.qblocks, q, row_start, kc,
-                                 vc, o, N, nq, nkv, p.keys_per_split, M, po, pml, s);
+    launch_attn_kernel<HD, true>(grid, dma, p.stages, p.key_halves, p.qblocks, p.key_tile, q,
+                                 row_start, kc, vc, o, N, nq, nkv, p.keys_per_split, M, po, pml,
+                                 s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t total = (size_t)M * nq * (HD / 4);
     const int gsz = (int)std::min<size_t>((total + 255) / 256, 8192);
     attn_combine_kernel<bf16_t><<<gsz, 256, 0, s>>>(po, pml, p.splits, M * nq, HD, (bf16_t*)o);
   } else {
-    launch_attn_kernel<HD, false>(grid, dma, p.stages, p.key_halves, p.qblocks, q, row_start, kc,
-                                  vc, o, N, nq, nkv, p.keys_per_split, M, nullptr, nullptr, s);
+    launch_attn_kernel<HD, false>(grid, dma, p.stages, p.key_halves, p.qblocks, p.key_tile, q,
+                                  row_start, kc, vc, o, N, nq, nkv, p.keys_per_split, M, nullptr,
+                                  nullptr, s);
   }
   return hipGetLastError();
 }
@@ -773,10 +797,11 @@ size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int h
 hipError_t launch_attention_cfg(int dtype, int M, int B, int N, int nq, int nkv, int hd,
                                 const void* q, const int32_t* row_start, const void* kc,
                                 const void* vc, void* o, void* ws, size_t ws_bytes, int splits,
-                                int stages, int key_halves, int qblocks, hipStream_t s) {
+                                int stages, int key_halves, int qblocks, int key_tile,
+                                hipStream_t s) {
   if (M <= 0) return hipSuccess;
   AttnPlan p = make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, stages, key_halves,
-                                  qblocks);
+                                  qblocks, key_tile);
   if (p.mfma && p.ws > ws_bytes) {
     p.splits = 1;
     p.keys_per_split = N;
@@ -802,11 +827,11 @@ hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int
                             const void* q, const int32_t* row_start, const void* kc,
                             const void* vc, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
   return launch_attention_cfg(dtype, M, B, N, nq, nkv, hd, q, row_start, kc, vc, o, ws, ws_bytes,
-                              0, 0, 0, 0, s);
+                              0, 0, 0, 0, 0, s);
 }
 
 size_t attention_cfg_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits) {
-  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, 0, 0, 0).ws;
+  return make_attn_plan_cfg(dtype, M, B, N, nq, nkv, hd, splits, 0, 0, 0, 0).ws;
 }
 
 }  // namespace dlm

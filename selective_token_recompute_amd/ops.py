@@ -154,9 +154,10 @@ def attention(q, row_start, kc, vc, nq, nkv, hd, o=None, ws=None):
 
 
 def attention_config(q, row_start, kc, vc, nq, nkv, hd, splits=0, stages=0, key_halves=0,
-                     qblocks=0, o=None):
+                     qblocks=0, key_tile=0, o=None):
     """attention() with a forced split-KV count, LDS stage count, key groups
-    (waves per 16-query block) and 16-query blocks per wave (0: the plan's)."""
+    (waves per 16-query block), 16-query blocks per wave and keys per LDS
+    tile (0: the plan's)."""
     M = q.shape[0]
     B, _, N, _ = kc.shape
     dt = _dt(q)
@@ -166,7 +167,7 @@ def attention_config(q, row_start, kc, vc, nq, nkv, hd, splits=0, stages=0, key_
     ws = _ws_cache(max(need, 256), q.device)
     L.check(L.lib().dlm_op_attention_config(dt, M, B, N, nq, nkv, hd, _p(q), _p(row_start), _p(kc),
                                             _p(vc), _p(o), splits, stages, key_halves, qblocks,
-                                            _p(ws),
+                                            key_tile, _p(ws),
                                             ws.numel(),
                                             _s()), "dlm_op_attention_config")
     return o

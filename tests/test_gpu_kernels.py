@@ -168,15 +168,16 @@ def test_attention_bf16_mfma(B, N, nq, nkv, hd, rows):
 ATTN_LAYOUTS = [(1, 1), (2, 1), (4, 1), (2, 2), (4, 2)]  # (key groups, query blocks per wave)
 
 
+@pytest.mark.parametrize("N", [320, 384])
 @pytest.mark.parametrize("splits", [0, 1, 2, 3, 8, 64])
 @pytest.mark.parametrize("stages", [2, 4])
 @pytest.mark.parametrize("layout", ATTN_LAYOUTS)
-def test_attention_forced_plans(splits, stages, layout):
-    """Every split-KV count (including more splits than 64-key tiles, which
-    the plan clamps, and a count that leaves a short last range), LDS depth
-    and wave layout, with two sequences of ragged row counts and GQA, against
-    the oracle."""
-    B, N, nq, nkv, hd = 2, 320, 8, 2, 128
+def test_attention_forced_plans(splits, stages, layout, N):
+    """Every split-KV count (including more splits than key tiles, which the
+    plan clamps, and a count that leaves a short last range), LDS depth and
+    wave layout, with two sequences of ragged row counts and GQA, against the
+    oracle; N = 320 runs 64-key tiles, N = 384 the 128-key tiles."""
+    B, nq, nkv, hd = 2, 8, 2, 128
     q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, [37, 70], seed=11)
     o = ops.attention_config(_dev(q.reshape(len(rs), nq * hd)), torch.from_numpy(rst).to(DEV),
                              _dev(kc), _dev(vc.transpose(0, 1, 3, 2)), nq, nkv, hd,
@@ -187,18 +188,19 @@ def test_attention_forced_plans(splits, stages, layout):
     assert (err <= 1e-2 + 2.0 ** -7 * np.abs(ref)).all(), err.max()
 
 
+@pytest.mark.parametrize("key_tile", [64, 128])
 @pytest.mark.parametrize("layout", ATTN_LAYOUTS)
 @pytest.mark.parametrize("B,N,nq,nkv,hd,rows", [
-    (1, 1024, 4, 4, 128, [200]),   # 16 key tiles, 4 query tiles (one partly filled)
+    (1, 1024, 4, 4, 128, [200]),   # 16 or 8 key tiles, 4 query tiles (one partly filled)
     (2, 256, 4, 1, 64, [100, 29]),  # hd 64, MQA: 4 queries per row share a wave
 ])
-def test_attention_wave_layouts(layout, B, N, nq, nkv, hd, rows):
-    """Each wave layout without a forced split, at hd 64 and 128, against the
-    oracle."""
+def test_attention_wave_layouts(layout, key_tile, B, N, nq, nkv, hd, rows):
+    """Each wave layout and key tile without a forced split, at hd 64 and
+    128, against the oracle."""
     q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, rows, seed=N + hd + layout[0])
     o = ops.attention_config(_dev(q.reshape(len(rs), nq * hd)), torch.from_numpy(rst).to(DEV),
                              _dev(kc), _dev(vc.transpose(0, 1, 3, 2)), nq, nkv, hd, splits=1,
-                             key_halves=layout[0], qblocks=layout[1])
+                             key_halves=layout[0], qblocks=layout[1], key_tile=key_tile)
     ref = oracle.unit_attention(q, rs, kc, vc).reshape(len(rs), nq * hd)
     err = np.abs(_f64(o) - ref)
     assert (err <= 1e-2 + 2.0 ** -7 * np.abs(ref)).all(), err.max()
