@@ -767,6 +767,8 @@ constexpr TileCfg kCfgs[] = {
     {128, 192, 2, 4, 3, 64, true},  // 42: 8 waves, 64x48 per wave, fragment prefetch
     {128, 192, 4, 2, 3, 64, true},  // 43: 8 waves, 32x96 per wave, fragment prefetch
     {96, 192, 2, 2, 3, 64},         // 44: 40 without fragment prefetch
+    {96, 192, 2, 6, 3, 64, true},   // 45: 12 waves, 48x32 per wave, fragment prefetch
+    {192, 192, 4, 3, 3, 64},        // 46: 12 waves, 48x64 per wave
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr bool cfgs_fit_lds() {
@@ -796,13 +798,16 @@ struct Plan {
 // 512, 8-wave tiles with fragment prefetch that give every CU one workgroup
 // (gate/up 192x192 at M = 384: 2 x 128 tiles; 128x192 at 128 < M <= 256:
 // 2 x 128 tiles, 4-13% ahead of the 192x128 and 256x128 tiles there); large M
-// favours 256x256 tiles with 8 waves.
+// favours 256x256 tiles with 8 waves.  The loop is bound by latency more than
+// by LDS bandwidth, so three waves per SIMD pay where the registers allow:
+// gate/up at 256 < M <= 320 runs the 12-wave 192x192 tile (4-5% ahead of the
+// 8-wave prefetch tile, level with it at M = 384).
 int pick_cfg(int M, int N, int K, bool dual) {
   static const int kBucket[] = {16, 32, 64, 128, 192, 256, 320, 384, 512};
   static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 36, 36, 8, 13};
   static const int kNarrowDeep[] = {7, 7, 1, 1, 6, 8, 36, 36, 37, 13};  // K >= 8192
   static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 37, 13};
-  static const int kDual[] = {1, 1, 1, 8, 43, 43, 35, 35, 13, 13};
+  static const int kDual[] = {1, 1, 1, 8, 43, 43, 46, 35, 13, 13};
   static const int kWide[] = {7, 7, 14, 10, 12, 13, 25, 25, 13, 13};
   int b = 0;
   while (b < 9 && M > kBucket[b]) ++b;
@@ -950,6 +955,8 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
     case 41: return run_mfma<64, 192, 2, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 42: return run_mfma<128, 192, 2, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 43: return run_mfma<128, 192, 4, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 45: return run_mfma<96, 192, 2, 6, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 46: return run_mfma<192, 192, 4, 3, 3, 64, EPI>(a, p, ep, ws, s);
     default: return run_mfma<96, 192, 2, 2, 3, 64, EPI>(a, p, ep, ws, s);
   }
 }
@@ -1047,7 +1054,7 @@ int pick_qkv_cfg(int M) {
   if (M <= 128) return 1;   // 64x128
   if (M <= 192) return 6;   // 96x128
   if (M <= 256) return 8;   // 128x128, 8 waves
-  if (M <= 384) return 44;  // 96x192, 4 waves
+  if (M <= 384) return 45;  // 96x192, 12 waves, prefetch: 8-12% ahead of 4 waves
   return 42;                // 128x192, 8 waves, fragment prefetch
 }
 
