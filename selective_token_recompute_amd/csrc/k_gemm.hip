@@ -800,14 +800,15 @@ struct Plan {
 // 2 x 128 tiles, 4-13% ahead of the 192x128 and 256x128 tiles there); large M
 // favours 256x256 tiles with 8 waves.  The loop is bound by latency more than
 // by LDS bandwidth, so three waves per SIMD pay where the registers allow:
-// gate/up at 256 < M <= 320 runs the 12-wave 192x192 tile (4-5% ahead of the
-// 8-wave prefetch tile, level with it at M = 384).
+// gate/up at 256 < M <= 384 runs the 12-wave 192x192 tile without prefetch
+// (4-5% ahead of the 8-wave prefetch tile at M = 288-320, 3% in the engine at
+// M = 384).
 int pick_cfg(int M, int N, int K, bool dual) {
   static const int kBucket[] = {16, 32, 64, 128, 192, 256, 320, 384, 512};
   static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 36, 36, 8, 13};
   static const int kNarrowDeep[] = {7, 7, 1, 1, 6, 8, 36, 36, 37, 13};  // K >= 8192
   static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 37, 13};
-  static const int kDual[] = {1, 1, 1, 8, 43, 43, 46, 35, 13, 13};
+  static const int kDual[] = {1, 1, 1, 8, 43, 43, 46, 46, 13, 13};
   static const int kWide[] = {7, 7, 14, 10, 12, 13, 25, 25, 13, 13};
   int b = 0;
   while (b < 9 && M > kBucket[b]) ++b;
