@@ -153,6 +153,8 @@ def _attn_case(B, N, nq, nkv, hd, rows_per_seq, seed, bf16=True):
     (3, 1024, 8, 2, 128, [5, 300, 77]),  # GQA, several sequences
     (2, 4096, 4, 4, 128, [9, 3]),
     (1, 256, 4, 1, 64, [100]),        # hd 64, MQA
+    (1, 1024, 32, 32, 128, [256]),    # default plan: four key groups on 128-key tiles
+    (1, 2048, 16, 16, 128, [256]),    # the same over two key splits
 ])
 def test_attention_bf16_mfma(B, N, nq, nkv, hd, rows):
     q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, rows, seed=N + nq)
