@@ -190,11 +190,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
   constexpr int RPI = 64 / CH;                 // tile rows per 1 KB load instruction
   constexpr int ROWS = BM + BN;                // tile rows per slice (A then B)
   constexpr int INSTR = ROWS / RPI;            // load instructions per slice
-  constexpr int IPW = INSTR / NW;              // per wave
+  // Instruction j of a slice is issued by wave j % NW: the first INSTR % NW
+  // waves issue IPW per slice, the others IPW_LO.  Every wave waits as if it
+  // issued IPW_LO, which is exact for the latter and, since a wave's loads
+  // complete in order, only waits for a few more of the newest loads in the
+  // former.
+  constexpr int IPW_LO = INSTR / NW;
+  constexpr int IPW = (INSTR + NW - 1) / NW;
+  constexpr bool EVEN = IPW == IPW_LO;
   constexpr int STAGE_BYTES = ROWS * RB;
   static_assert(BK == 32 || BK == 64, "k-slice");
-  static_assert(ROWS % RPI == 0 && INSTR % NW == 0,
-                "load instructions must split evenly over the waves");
+  static_assert(ROWS % RPI == 0 && IPW_LO >= 1,
+                "every wave issues at least one load instruction per slice");
   static_assert((STAGES - 1) * IPW < 64, "in-flight loads must fit the vmcnt counter");
   static_assert(!DUAL || (TN % 2 == 0), "dual tiles need an even number of column tiles");
   static_assert(STAGES >= 2 && STAGES <= 8, "stages");
@@ -221,7 +228,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
   const bf16_t* src[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int j = wave + i * NW;                   // instruction index within the slice
+    // instruction index within the slice (a wave's missing last one, never
+    // issued, points at the slice's last row)
+    const int j = min(wave + i * NW, INSTR - 1);
     const int r = j * RPI + lane / CH;             // tile row (A rows then B rows)
     const int chunk = (lane % CH) ^ slot_xor<CH>(r);  // global chunk for this slot
     const bf16_t* base;
@@ -245,12 +254,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
     }
     src[i] = base + kbeg + chunk * 8;
   }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int kt) {
     unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int j = wave + i * NW;
-      dma16(src[i] + kt * BK, st + j * 1024);
+      const int j = wave_u + i * NW;
+      if (EVEN || i < IPW_LO || j < INSTR) dma16(src[i] + kt * BK, st + j * 1024);
     }
   };
 
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < KT) issue(s);
     for (int kt = 0; kt < KT; ++kt) {
-      wait_slices<IPW, STAGES - 1>(min(STAGES - 2, KT - 1 - kt));
+      wait_slices<IPW_LO, STAGES - 1>(min(STAGES - 2, KT - 1 - kt));
       lds_barrier();
       if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
       Frags f;
@@ -345,7 +355,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
     for (int s = 0; s < 3; ++s)
       if (s < KT) issue(s);
     if (KT > 0) {
-      wait_slices<IPW, 3>(min(2, KT - 1));
+      wait_slices<IPW_LO, 3>(min(2, KT - 1));
       lds_barrier();
       read_frags(0, f0);
       wait_lgkm0();
@@ -354,7 +364,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
     // load overwrites any more, so that the reads and the MFMAs stay in one
     // block), slice kt+3 is issued while kt + 3 < KT
     auto step = [&](int kt, Frags& cur, Frags& nxt) __attribute__((always_inline)) {
-      wait_slices<IPW, 3>(min(1, max(0, KT - 2 - kt)));
+      wait_slices<IPW_LO, 3>(min(1, max(0, KT - 2 - kt)));
       lds_barrier();
       if (kt + 3 < KT) issue(kt + 3);
       read_frags(min(kt + 1, KT - 1), nxt);
@@ -769,6 +779,9 @@ constexpr TileCfg kCfgs[] = {
     {96, 192, 2, 2, 3, 64},         // 44: 40 without fragment prefetch
     {96, 192, 2, 6, 3, 64, true},   // 45: 12 waves, 48x32 per wave, fragment prefetch
     {192, 192, 4, 3, 3, 64},        // 46: 12 waves, 48x64 per wave
+    {192, 128, 3, 4, 3, 64, true},  // 47: 12 waves, 64x32 per wave, fragment prefetch
+    {192, 128, 6, 2, 3, 64, true},  // 48: 12 waves, 32x64 per wave, fragment prefetch
+    {128, 192, 4, 3, 3, 64, true},  // 49: 12 waves, 32x64 per wave, fragment prefetch
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr bool cfgs_fit_lds() {
@@ -802,13 +815,15 @@ struct Plan {
 // by LDS bandwidth, so three waves per SIMD pay where the registers allow:
 // gate/up at 256 < M <= 384 runs the 12-wave 192x192 tile without prefetch
 // (4-5% ahead of the 8-wave prefetch tile at M = 288-320, 3% in the engine at
-// M = 384).
+// M = 384), gate/up at 128 < M <= 256 the 12-wave 128x192 prefetch tile (2-5%
+// ahead of 8 waves), O at 256 < M <= 384 and down at 256 < M <= 320 the
+// 12-wave 192x128 prefetch tile (1-4% ahead; level for down at M = 384).
 int pick_cfg(int M, int N, int K, bool dual) {
   static const int kBucket[] = {16, 32, 64, 128, 192, 256, 320, 384, 512};
-  static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 36, 36, 8, 13};
-  static const int kNarrowDeep[] = {7, 7, 1, 1, 6, 8, 36, 36, 37, 13};  // K >= 8192
+  static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 47, 47, 8, 13};
+  static const int kNarrowDeep[] = {7, 7, 1, 1, 6, 8, 47, 36, 37, 13};  // K >= 8192
   static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 37, 13};
-  static const int kDual[] = {1, 1, 1, 8, 43, 43, 46, 46, 13, 13};
+  static const int kDual[] = {1, 1, 1, 8, 49, 49, 46, 46, 13, 13};
   static const int kWide[] = {7, 7, 14, 10, 12, 13, 25, 25, 13, 13};
   int b = 0;
   while (b < 9 && M > kBucket[b]) ++b;
@@ -958,6 +973,9 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
     case 43: return run_mfma<128, 192, 4, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 45: return run_mfma<96, 192, 2, 6, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 46: return run_mfma<192, 192, 4, 3, 3, 64, EPI>(a, p, ep, ws, s);
+    case 47: return run_mfma<192, 128, 3, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 48: return run_mfma<192, 128, 6, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 49: return run_mfma<128, 192, 4, 3, 3, 64, EPI, true>(a, p, ep, ws, s);
     default: return run_mfma<96, 192, 2, 2, 3, 64, EPI>(a, p, ep, ws, s);
   }
 }

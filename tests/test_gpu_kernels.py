@@ -558,7 +558,7 @@ def test_rope_scatter(bf16):
     assert (np.moveaxis(vcn, 3, 2)[np.broadcast_to(~touched[:, None, :], kcn.shape[:3])] == 3.0).all()
 
 
-@pytest.mark.parametrize("cfg", [35, 36, 37, 38, 39, 40, 41, 42, 43, 45])
+@pytest.mark.parametrize("cfg", [35, 36, 37, 38, 39, 40, 41, 42, 43, 45, 47, 48, 49])
 @pytest.mark.parametrize("epi", [L.DLM_EPI_STORE_F32, L.DLM_EPI_SWIGLU])
 def test_gemm_prefetch_tiles_long_k(cfg, epi):
     """The fragment-prefetch tiles over a long K (64 k-slices: the steady
@@ -584,7 +584,7 @@ def test_gemm_prefetch_tiles_long_k(cfg, epi):
 # every tile configuration but 13 (256x256 with a 2-slice ring: one wave row
 # of fp32 results does not fit its LDS, so the op refuses it); tiles of 64,
 # 192 and 256 columns split or straddle heads
-QKV_CFGS = [c for c in range(47) if c != 13]
+QKV_CFGS = [c for c in range(50) if c != 13]
 
 
 def test_gemm_qkv_refuses_oversized_tile():
