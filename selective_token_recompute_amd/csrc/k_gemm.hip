@@ -782,6 +782,8 @@ constexpr TileCfg kCfgs[] = {
     {192, 128, 3, 4, 3, 64, true},  // 47: 12 waves, 64x32 per wave, fragment prefetch
     {192, 128, 6, 2, 3, 64, true},  // 48: 12 waves, 32x64 per wave, fragment prefetch
     {128, 192, 4, 3, 3, 64, true},  // 49: 12 waves, 32x64 per wave, fragment prefetch
+    {256, 192, 4, 3, 2, 64},        // 50: 12 waves, 64x64 per wave
+    {256, 192, 4, 2, 2, 64},        // 51: 8 waves, 64x96 per wave
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr bool cfgs_fit_lds() {
@@ -817,16 +819,18 @@ struct Plan {
 // (4-5% ahead of the 8-wave prefetch tile at M = 288-320, 3% in the engine at
 // M = 384), gate/up at 128 < M <= 256 the 12-wave 128x192 prefetch tile (2-5%
 // ahead of 8 waves), O at 256 < M <= 384 and down at 256 < M <= 320 the
-// 12-wave 192x128 prefetch tile (1-4% ahead; level for down at M = 384).
+// 12-wave 192x128 prefetch tile (1-4% ahead; level for down at M = 384), and
+// gate/up at 384 < M <= 1536 the 12-wave 256x192 tile (one workgroup per CU
+// at M = 512; 10-16% ahead of 256x256, which wins again from M = 2048).
 int pick_cfg(int M, int N, int K, bool dual) {
-  static const int kBucket[] = {16, 32, 64, 128, 192, 256, 320, 384, 512};
-  static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 47, 47, 8, 13};
-  static const int kNarrowDeep[] = {7, 7, 1, 1, 6, 8, 47, 36, 37, 13};  // K >= 8192
-  static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 37, 13};
-  static const int kDual[] = {1, 1, 1, 8, 49, 49, 46, 46, 13, 13};
-  static const int kWide[] = {7, 7, 14, 10, 12, 13, 25, 25, 13, 13};
+  static const int kBucket[] = {16, 32, 64, 128, 192, 256, 320, 384, 512, 1536};
+  static const int kNarrow[] = {7, 7, 1, 1, 6, 8, 47, 47, 8, 13, 13};
+  static const int kNarrowDeep[] = {7, 7, 1, 1, 6, 8, 47, 36, 37, 13, 13};  // K >= 8192
+  static const int kMedium[] = {7, 7, 14, 1, 6, 8, 5, 5, 37, 13, 13};
+  static const int kDual[] = {1, 1, 1, 8, 49, 49, 46, 46, 50, 50, 13};
+  static const int kWide[] = {7, 7, 14, 10, 12, 13, 25, 25, 13, 13, 13};
   int b = 0;
-  while (b < 9 && M > kBucket[b]) ++b;
+  while (b < 10 && M > kBucket[b]) ++b;
   if (dual) return kDual[b];
   if (N <= 8192) return K >= 8192 ? kNarrowDeep[b] : kNarrow[b];
   if (N <= 32768) return kMedium[b];
@@ -976,6 +980,8 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
     case 47: return run_mfma<192, 128, 3, 4, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 48: return run_mfma<192, 128, 6, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 49: return run_mfma<128, 192, 4, 3, 3, 64, EPI, true>(a, p, ep, ws, s);
+    case 50: return run_mfma<256, 192, 4, 3, 2, 64, EPI>(a, p, ep, ws, s);
+    case 51: return run_mfma<256, 192, 4, 2, 2, 64, EPI>(a, p, ep, ws, s);
     default: return run_mfma<96, 192, 2, 2, 3, 64, EPI>(a, p, ep, ws, s);
   }
 }

@@ -584,7 +584,7 @@ def test_gemm_prefetch_tiles_long_k(cfg, epi):
 # every tile configuration but 13 (256x256 with a 2-slice ring: one wave row
 # of fp32 results does not fit its LDS, so the op refuses it); tiles of 64,
 # 192 and 256 columns split or straddle heads
-QKV_CFGS = [c for c in range(50) if c != 13]
+QKV_CFGS = [c for c in range(52) if c != 13]
 
 
 def test_gemm_qkv_refuses_oversized_tile():
