@@ -135,36 +135,74 @@ typedef struct {
 typedef struct dlm_handle dlm_handle;
 
 /* Bytes of state_mem needed for this model and run; 0 if the descriptors are
- * invalid. */
+ * invalid.  The block holds everything the method keeps between steps: the
+ * per-layer K/V cache of every position (SureLock page, §2 Methodology, core
+ * mechanism: locked positions keep their cached K and V), the previous
+ * step's posterior of every position (§2 locking condition: the KL test
+ * compares p_t with p_{t-1}), tokens, lock bits and counters, plus the
+ * activations of at most batch*seq_len active rows and kernel workspace. */
 size_t dlm_state_bytes(const dlm_model_desc* model, const dlm_run_desc* run);
 
-/* Validates the descriptors, carves state_mem, zeroes the lock bits, counters
+/* Starts a decoding run (SureLock page, §1 Problem Statement: a masked
+ * diffusion LM denoises the whole sequence over T steps; §2 Methodology:
+ * every position starts active, the active set A_0 is all of them).
+ * Validates the descriptors, carves state_mem, zeroes the lock bits, counters
  * and flags, writes tokens (prompt then mask_id) and builds the rotary table.
- * prompt_tokens: device int32 [batch][prompt_len].  hip_stream: a hipStream_t
- * (NULL: the default stream).  Enqueued on the stream; *out receives a
- * host-allocated handle freed by dlm_destroy. */
+ * model, weights, run: host structs, read during the call (the weight
+ * pointers are kept).  prompt_tokens: device int32 [batch][prompt_len]
+ * (may be NULL when prompt_len == 0).  state_mem: caller-owned device memory
+ * of at least dlm_state_bytes() bytes, 256-byte aligned; its contents need
+ * not be initialised and it must outlive the handle.  hip_stream: a
+ * hipStream_t (NULL: the default stream).  Enqueued on the stream; *out
+ * receives a host-allocated handle freed by dlm_destroy.  Errors:
+ * DLM_E_INVALID (bad descriptor, null or misaligned pointer), DLM_E_SIZE
+ * (state_bytes too small), DLM_E_HIP (a launch failed; no handle). */
 int dlm_step_init(const dlm_model_desc* model, const dlm_weights* weights,
                   const dlm_run_desc* run, const int32_t* prompt_tokens, void* state_mem,
                   size_t state_bytes, void* hip_stream, dlm_handle** out);
 
-/* One denoising iteration over the active positions: compaction of the
- * active set from the lock bitmask, then per layer RMSNorm, QKV projection,
- * rotary embedding and K/V scatter into the cache, attention of the active
- * queries over all seq_len cached positions, out-projection, SwiGLU FFN; then
- * final norm, LM head and the vocabulary statistics (log-normaliser, argmax,
+/* One denoising iteration over the active positions (SureLock page, §2
+ * Methodology: permanent deactivation -- locked positions get no query
+ * projection and no FFN; continued attention -- the active queries attend
+ * to every position through the cached K/V, fresh Q/K/V only for the active
+ * subset; algorithmic complexity -- attention O(M_t N d), FFN O(M_t d^2)):
+ * compaction of the active set from the lock bitmask, then per layer
+ * RMSNorm, QKV projection, rotary embedding and K/V scatter into the cache,
+ * attention of the active queries over all seq_len cached positions,
+ * out-projection, SwiGLU FFN; then final norm, LM head and the vocabulary
+ * statistics the locking condition needs (log-normaliser, argmax,
  * max-probability confidence, KL against the previous step's posterior).
  * Synchronises the stream once (to read the active count).  *m_tot_out (if
- * non-null) receives the number of active rows.  DLM_E_STATE if a step is
- * pending its dlm_lock_update or all steps were taken. */
+ * non-null) receives the number of active rows.  Errors: DLM_E_STATE if a
+ * step is pending its dlm_lock_update or all steps were taken; DLM_E_NUMERIC
+ * if the previous step latched a non-finite posterior (nothing launched);
+ * DLM_E_HIP if a launch failed (the state is then undefined). */
 int dlm_step(dlm_handle* h, int32_t* m_tot_out);
 
-/* State transition after dlm_step: commit (unmask) the top-k, then the lock
- * test and the monotone bitmask update; ov (nullable) replays given
- * decisions.  Asynchronous except for the copy of override arrays. */
+/* State transition after dlm_step.  Commit: the top-k most confident masked
+ * positions of the current semi-autoregressive block take their argmax
+ * (SlowFast page, "Accelerating Diffusion LLMs with SlowFast Sampling", §1
+ * confidence-based selection in semi-autoregressive blocks, §2 top-k; or
+ * SlowFast's two-stage cycle, §2 two-stage pipeline, with sampler
+ * DLM_SAMPLER_SLOWFAST).  Lock: the KL test with the confidence gate and the
+ * monotone bitmask update (SureLock page, §2 Methodology: locking condition
+ * KL(p_t || p_{t-1}) <= eps with an optional confidence gate; permanent
+ * deactivation).  ov (nullable, host memory) replays given decisions in
+ * place of the rule (see dlm_override).  If the step latched a non-finite
+ * posterior, neither commits nor locks happen (the error is returned by the
+ * next dlm_step).  Asynchronous except for the copy of override arrays.
+ * Errors: DLM_E_STATE without a pending step; DLM_E_INVALID for an
+ * out-of-range override entry (checked before any launch). */
 int dlm_lock_update(dlm_handle* h, const dlm_override* ov);
 
 /* Device pointer and element count of a state array (aliases state_mem;
- * valid until the next dlm_step or dlm_lock_update). */
+ * valid until the next dlm_step or dlm_lock_update; read-only for the
+ * caller except through the documented replay path).  The arrays are the
+ * method's per-step quantities (SureLock page, §2 Methodology): tokens, the
+ * lock bitmask and counters, the active set A_t (row sequence / position),
+ * the posterior statistics of the locking condition (argmax, confidence,
+ * KL, log-normaliser, logits) and the per-layer K/V cache.  Errors:
+ * DLM_E_INVALID for an unknown `what` or null outputs. */
 enum {
   DLM_GET_TOKENS = 0,    /* int32  [batch][seq_len] */
   DLM_GET_LOCK_BITS = 1, /* uint64 [batch][ceil(seq_len/64)] */
@@ -188,8 +226,10 @@ enum {
 };
 int dlm_get(dlm_handle* h, int32_t what, const void** dev_ptr, int64_t* n);
 
-/* Host-side counters of the last dlm_step: its step index and algorithmic
- * FLOPs (sum over the GEMM and attention launches it made). */
+/* Host-side counters of the last dlm_step: its step index, active count and
+ * algorithmic FLOPs, the sum over the GEMM and attention launches it made
+ * (SureLock page, §2 algorithmic complexity: projections and FFN on M_t
+ * rows, attention of M_t queries over N keys, plus the LM head). */
 int dlm_last_step_info(const dlm_handle* h, int32_t* step, int32_t* m_tot, double* flops);
 
 /* Frees the handle (not state_mem).  Waits for the stream. */

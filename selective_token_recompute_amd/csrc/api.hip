@@ -534,6 +534,7 @@ int dlm_lock_update(dlm_handle* h, const dlm_override* ov) {
   la.frozen = h->at<uint64_t>(y.frozen);
   la.has_prev = h->at<int32_t>(y.has_prev);
   la.sf_state = h->at<int32_t>(y.sf_state);
+  la.err = h->at<int32_t>(y.ctl) + 1;
   if (la.do_commit || la.do_lock)
     TRY(timed(h, DLM_K_COMMIT_LOCK, 0.0, 0.0, [&] { return launch_commit_lock(la, h->stream); }));
   if (ov && (ov_commit || ov_lock)) {

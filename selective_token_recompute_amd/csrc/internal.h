@@ -148,6 +148,9 @@ struct LockArgs {
   uint64_t* frozen;
   int32_t* has_prev;
   int32_t* sf_state;
+  // nullable: the device word the statistics latch on a non-finite
+  // log-normaliser; while it is set the kernel commits and locks nothing
+  const int32_t* err;
 };
 constexpr int kSfStateInts = 16;  // phase, lo, hi, slow_n, hist_n, hist[8], 3 unused
 hipError_t launch_commit_lock(const LockArgs& a, hipStream_t s);

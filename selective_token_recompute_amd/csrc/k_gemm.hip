@@ -783,7 +783,6 @@ constexpr TileCfg kCfgs[] = {
     {192, 128, 6, 2, 3, 64, true},  // 48: 12 waves, 32x64 per wave, fragment prefetch
     {128, 192, 4, 3, 3, 64, true},  // 49: 12 waves, 32x64 per wave, fragment prefetch
     {256, 192, 4, 3, 2, 64},        // 50: 12 waves, 64x64 per wave
-    {256, 192, 4, 2, 2, 64},        // 51: 8 waves, 64x96 per wave
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr bool cfgs_fit_lds() {
@@ -981,7 +980,6 @@ hipError_t dispatch_mfma(const GemmArgs& a, const Plan& p, EpiParams ep, void* w
     case 48: return run_mfma<192, 128, 6, 2, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 49: return run_mfma<128, 192, 4, 3, 3, 64, EPI, true>(a, p, ep, ws, s);
     case 50: return run_mfma<256, 192, 4, 3, 2, 64, EPI>(a, p, ep, ws, s);
-    case 51: return run_mfma<256, 192, 4, 2, 2, 64, EPI>(a, p, ep, ws, s);
     default: return run_mfma<96, 192, 2, 2, 3, 64, EPI>(a, p, ep, ws, s);
   }
 }

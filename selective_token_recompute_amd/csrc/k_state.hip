@@ -272,6 +272,9 @@ __global__ __launch_bounds__(kLockThreads) void commit_lock_kernel(LockArgs a) {
   const int N = a.N, W = (N + 63) >> 6;
   const int r0 = a.row_start[b], r1 = a.row_start[b + 1];
   int32_t* tok = a.tokens + (size_t)b * N;
+  // a step whose posterior was non-finite decides nothing: its argmax and
+  // statistics are not meaningful (the error is reported by the next step)
+  if (a.err && *a.err) return;
 
   if (a.do_commit && a.sampler == 1) {
     __shared__ int s_front, e_max;

@@ -4,12 +4,21 @@ Each step runs on both sides from the same state.  Logits and statistics are
 compared within tolerance; the commit and lock decisions must match bit for
 bit, except where the oracle's own decision sits inside a margin (near-tied
 argmax or confidence ranking, or a lock comparison within 1e-3 of its
-threshold): there the oracle's decision is replayed into the engine through
-the lock-update override and the replay is counted.
+threshold): there the engine first takes its own decision through
+dlm_lock_update, the difference is checked against those margins, and then
+the oracle's tokens, lock bits and counters are written over the engine's
+state arrays (tensor copies into the state block, not the ABI override;
+the override path has its own test) and the replay is counted.
+
+``record`` appends a JSON line per run to the file named by the environment
+variable DLM_PARITY_RECORD (nothing is written when it is unset), so that
+replay counts survive pytest's output capture.
 """
 from __future__ import annotations
 
 import dataclasses
+import json
+import os
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -33,6 +42,43 @@ class StepReport:
     argmax_mismatch_near_tie: int
     max_dconf: float
     max_dkl: float
+    # the oracle's k-th / (k+1)-th confidence gap among this step's commit
+    # candidates (inf when the count decides nothing) and whether it lies
+    # within the confidence error of the step (an ambiguous ranking)
+    commit_gap: float = float("inf")
+    commit_ambiguous: bool = False
+
+
+def record(name: str, reps: List["StepReport"], **extra) -> Dict:
+    """Summary of a lockstep run (steps, replays by reason, largest logit
+    error against its scale); appended as one JSON line to
+    $DLM_PARITY_RECORD when that variable is set."""
+    reasons: Dict[str, int] = {}
+    for r in reps:
+        for why in r.reasons:
+            reasons[why] = reasons.get(why, 0) + 1
+    rel = [r.max_dz / r.z_scale for r in reps if r.z_scale > 0]
+    out = dict(name=name, steps=len(reps), replays=sum(r.replayed for r in reps),
+               replay_reasons=reasons, argmax_near_tie_rows=sum(r.argmax_mismatch_near_tie
+                                                                for r in reps),
+               ambiguous_commit_steps=sum(r.commit_ambiguous for r in reps),
+               max_dconf=max((r.max_dconf for r in reps), default=0.0),
+               max_dz=max((r.max_dz for r in reps), default=0.0),
+               max_dz_rel=max(rel, default=0.0), m_trace=[r.m for r in reps])
+    out.update(extra)
+    append_record(out)
+    print(f"\n[{name}] steps={out['steps']} replays={out['replays']} {reasons} "
+          f"max|dz|/scale={out['max_dz_rel']:.3g}", flush=True)
+    return out
+
+
+def append_record(entry: Dict) -> None:
+    """Appends one JSON line to $DLM_PARITY_RECORD (no-op when unset)."""
+    path = os.environ.get("DLM_PARITY_RECORD")
+    if path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "a") as f:
+            f.write(json.dumps(entry) + "\n")
 
 
 def bits_to_bool(bits: np.ndarray, N: int) -> np.ndarray:
@@ -63,6 +109,13 @@ def top2_gap(z: np.ndarray, mask_id: int) -> np.ndarray:
     zz[:, mask_id] = -np.inf
     part = np.partition(zz, -2, axis=1)
     return part[:, -1] - part[:, -2]
+
+
+def _kth_gap(c, k: int) -> float:
+    """Gap between the k-th and (k+1)-th largest values (inf when a top-k
+    of these values decides nothing)."""
+    c = np.sort(np.asarray(c, np.float64))[::-1]
+    return float(c[k - 1] - c[k]) if 0 < k < len(c) else float("inf")
 
 
 def explain_difference(shape, run, lock, t, x_before, x_g, x_o, lk_g, lk_o, cnt_g, cnt_o,
@@ -133,7 +186,8 @@ def run_lockstep(shape, W: Dict, run, lock: Dict, prompts: np.ndarray, steps: Op
         zg = eng.logits().cpu().numpy()[rs, rp]
         fin = np.isfinite(zo)
         assert np.array_equal(fin, np.isfinite(zg)), f"step {t}: -inf pattern"
-        dz = np.abs(np.where(fin, zg - zo, 0.0))
+        with np.errstate(invalid="ignore"):  # -inf - -inf at the mask column
+            dz = np.abs(np.where(fin, zg - zo, 0.0))
         scale = float(np.abs(zo[fin]).max())
         max_dz = float(dz.max())
         if check:
@@ -157,7 +211,16 @@ def run_lockstep(shape, W: Dict, run, lock: Dict, prompts: np.ndarray, steps: Op
         if check and hk.any():
             assert (dkl <= kl_tol).all(), f"step {t}: KL max diff {dkl.max():.3g}"
 
+        # the oracle's commit ranking at the k-th / (k+1)-th candidate
+        sch = oracle.unit_schedule(run, t)
+        cand = (pos_o >= sch["lo"]) & (pos_o < sch["hi"]) & \
+            (x_before[seq_o, pos_o] == shape.mask_id)
+        gaps = [_kth_gap(so["conf"][cand & (seq_o == b)], sch["k"]) for b in range(B)]
+        commit_gap = min(gaps) if gaps else float("inf")
+        conf_tol = 2.0 * float(dconf.max()) + 1e-7
+
         # oracle decision (the authority), then the engine's own decision
+        locked_before, cnt_before = orc.locked(), orc.counters()
         orc.lock_update()
         x_o, lk_o, cnt_o = orc.tokens(), orc.locked(), orc.counters()
         cs, cp, ct = orc.commits()
@@ -167,6 +230,20 @@ def run_lockstep(shape, W: Dict, run, lock: Dict, prompts: np.ndarray, steps: Op
         x_g = tok_v.cpu().numpy()
         lk_g = bits_to_bool(bits_v.cpu().numpy().view(np.uint64), N)
         cnt_g = cnt_v.cpu().numpy()
+        # every step: the engine's transition is exactly the rule (the
+        # oracle's, applied to the engine's own statistics with the float32
+        # thresholds the engine compares against), so any difference from
+        # the oracle's decision comes from the statistics alone
+        lock32 = dict(lock, kl_eps=float(np.float32(lock["kl_eps"])),
+                      conf_tau=float(np.float32(lock["conf_tau"])))
+        assert lock.get("sampler", "semi_ar") == "semi_ar", "SlowFast runs have their own harness"
+        rx, rl, rc = oracle.unit_lock_transition(
+            shape, run, lock32, t, rs, rp, rr.astype(np.uint8), sg["argmax"],
+            sg["conf"].astype(np.float64), sg["kl"].astype(np.float64),
+            sg["has_kl"].astype(np.uint8), x_before, locked_before, cnt_before)
+        assert np.array_equal(rx, x_g), f"step {t}: commit is not the rule on the engine's stats"
+        assert np.array_equal(rl, lk_g) and np.array_equal(rc, cnt_g), \
+            f"step {t}: lock update is not the rule on the engine's stats"
         reasons = []
         if not (np.array_equal(x_g, x_o) and np.array_equal(lk_g, lk_o)
                 and np.array_equal(cnt_g, cnt_o)):
@@ -182,6 +259,6 @@ def run_lockstep(shape, W: Dict, run, lock: Dict, prompts: np.ndarray, steps: Op
         replay = bool(reasons)
         reports.append(StepReport(t, orc.m, max_dz, scale, replay, reasons,
                                   int((am_bad & near_tie).sum()), float(dconf.max()),
-                                  float(dkl.max())))
+                                  float(dkl.max()), commit_gap, commit_gap <= conf_tol))
     eng.close()
     return reports

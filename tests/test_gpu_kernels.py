@@ -79,9 +79,12 @@ def test_gemm_resid_add_bf16(M, N, K):
     assert err <= 2e-5 * max(1.0, np.abs(ref).max()), err
 
 
-@pytest.mark.parametrize("M", [1, 16, 33, 100, 384])
-def test_gemm_swiglu_bf16(M):
-    N, K = 320, 512
+@pytest.mark.parametrize("M,N,K", [(1, 320, 512), (16, 320, 512), (33, 320, 512),
+                                   (100, 320, 512), (384, 320, 512),
+                                   # the 12-wave 256x192 tile of 384 < M <= 1536 at the
+                                   # model's K: ragged M, several k-slices
+                                   (385, 384, 4096), (700, 384, 4096), (1536, 384, 4096)])
+def test_gemm_swiglu_bf16(M, N, K):
     A, Wg, Wu = _gemm_inputs(M, N, K, seed=7 * M)
     U = ops.gemm(L.DLM_EPI_SWIGLU, _dev(A), _dev(Wg), W2=_dev(Wu))
     g = oracle.unit_linear(A, Wg)
@@ -584,7 +587,7 @@ def test_gemm_prefetch_tiles_long_k(cfg, epi):
 # every tile configuration but 13 (256x256 with a 2-slice ring: one wave row
 # of fp32 results does not fit its LDS, so the op refuses it); tiles of 64,
 # 192 and 256 columns split or straddle heads
-QKV_CFGS = [c for c in range(52) if c != 13]
+QKV_CFGS = [c for c in range(ops.num_gemm_configs()) if c != 13]
 
 
 def test_gemm_qkv_refuses_oversized_tile():

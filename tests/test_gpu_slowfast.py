@@ -5,10 +5,13 @@
 * The engine in lockstep with the oracle (its own forward pass and rule) at
   a small fp32 width and a bf16 width with two sequences, with a setting
   that freezes positions and brings them back: active rows (frozen positions
-  absent), logits, statistics (no KL for a position back from frozen), then
-  tokens, locks, frozen set, cycle state and previous-posterior flags bit
-  for bit, the oracle's decision replayed only where it sits within the
-  step's confidence difference of a tie or threshold.
+  absent), logits, argmax, confidence and KL (none for a position back from
+  frozen), then tokens, locks, frozen set, cycle state and previous-posterior
+  flags bit for bit.  A differing step is accepted only if the oracle's rule
+  on the engine's own statistics gives the engine's decision and the
+  oracle's decision sits within twice the step's confidence difference of a
+  comparison the rule made at that step (k-th / (k+1)-th candidate, a
+  threshold); the oracle's decision is then replayed and counted.
 * The bench's slowfast setting at the full LLaDA-8B shape: invariants.
 """
 import numpy as np
@@ -20,7 +23,7 @@ import synth
 from selective_token_recompute_amd import _lib as L
 from selective_token_recompute_amd import engine as E
 from selective_token_recompute_amd import ops
-from tests.harness import bits_to_bool, logit_tol
+from tests.harness import MARGIN, append_record, bits_to_bool, logit_tol, top2_gap
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -132,41 +135,86 @@ def _engineered_lock(W, shape, run, prompts, **kw):
     return _lock(sf_whist=1, sf_tau_conv=best[1], sf_tau_high=1.0, **kw), best[0]
 
 
-def _sf_margin(orc, lock, shape, so):
-    """Smallest distance, over this step's masked rows, between confidences
-    of one sequence or between a confidence and a SlowFast threshold: the
-    margin of the step's commit decisions."""
-    rs, rp, _ = orc.rows()
-    masked = orc.tokens()[rs, rp] == shape.mask_id
+def _kth_gap(c, k):
+    """Confidence gap between the k-th and (k+1)-th of a descending ranking
+    (infinite when the ranking does not decide anything)."""
+    c = np.sort(np.asarray(c, np.float64))[::-1]
+    return float(c[k - 1] - c[k]) if 0 < k < len(c) else np.inf
+
+
+def _sf_decision_margin(run, lock, mask_id, pos, conf, x, st_before, st_after):
+    """Margin of one sequence's SlowFast commit decision at this step: the
+    distance of the oracle's statistics to each comparison the rule makes.
+    Exploratory stage: the end point (largest candidate position with conf >=
+    sf_tau_conv) moves only if the candidate at it drops below the threshold
+    or one beyond it reaches it; the top-sf_k choice in the window turns on
+    the k-th / (k+1)-th gap.  Accelerated commit (this step's span): the
+    count of in-span candidates above sf_tau_high and, when it falls short
+    of sf_k, the k-th / (k+1)-th gap in the span.  The variance test compares
+    integer end points and has no margin of its own."""
+    cand = x[pos] == mask_id
+    cpos, cconf = pos[cand], conf[cand].astype(np.float64)
+    if len(cpos) == 0:
+        return np.inf
+    k = int(lock["sf_k"])
+    s = int(cpos.min())
     m = np.inf
-    for b in np.unique(rs[masked]):
-        c = np.sort(so["conf"][masked & (rs == b)])
-        if len(c) > 1:
-            m = min(m, float(np.diff(c).min()))
-        m = min(m, float(np.abs(c - lock["sf_tau_conv"]).min()),
-                float(np.abs(c - lock["sf_tau_high"]).min()))
+    if st_before[0] == 0:
+        tau = float(lock["sf_tau_conv"])
+        hit = cconf >= tau
+        rel = cpos >= cpos[hit].max() if hit.any() else np.ones(len(cpos), bool)
+        m = min(m, float(np.abs(cconf[rel] - tau).min()))
+        m = min(m, _kth_gap(cconf[cpos < s + run.block_len], k))
+    span = None
+    if st_before[0] == 1:
+        span = (st_before[1], st_before[2])
+    elif st_after[0] == 1:
+        span = (st_after[1], st_after[2])
+    if span is not None:
+        ins = (cpos >= span[0]) & (cpos < span[1])
+        if ins.any():
+            m = min(m, float(np.abs(cconf[ins] - float(lock["sf_tau_high"])).min()))
+            m = min(m, _kth_gap(cconf[ins], k))
     return m
+
+
+def _rule_on(run, lock, mask_id, rs, rp, argmax, conf, x, frozen, has_prev, state):
+    """The oracle's SlowFast rule applied, sequence by sequence, to the given
+    statistics from the given pre-update state."""
+    x, frozen, has_prev, state = x.copy(), frozen.copy(), has_prev.copy(), state.copy()
+    for b in range(x.shape[0]):
+        sel = rs == b
+        _, x[b], frozen[b], has_prev[b], state[b] = oracle.unit_slowfast(
+            run, lock, mask_id, rp[sel], argmax[sel], conf[sel], x[b], frozen[b], has_prev[b],
+            state[b])
+    return x, frozen, has_prev, state
 
 
 def run_slowfast_lockstep(shape, W, run, lock, prompts):
     """Every step on both sides from the same state: active rows (the frozen
-    positions absent), logits and statistics within tolerance; then the
-    commit decision, frozen set, cycle state and previous-posterior flags bit
-    for bit, except where the oracle's own decision sits within twice the
-    step's confidence difference of a tie or a threshold: there the oracle's
-    decision is written into the engine's state and counted."""
+    positions absent), logits, argmax (differences only at near ties),
+    confidence and KL within tolerance; then the commit decision, frozen set,
+    cycle state and previous-posterior flags bit for bit.  Where they differ,
+    (a) the oracle's rule applied to the engine's own statistics must give
+    the engine's decision exactly (so the difference comes from the
+    statistics alone), and (b) the oracle's decision must sit within twice
+    the step's largest confidence difference of one of the comparisons the
+    rule made at this step; lock differences must sit within the lock-test
+    margin.  Then the oracle's decision is written into the engine's state
+    and counted as a replay."""
     dw = E.upload_weights(W, shape, DEV)
     pr = torch.from_numpy(prompts).to(DEV)
     eng = E.Engine(shape, dw, run, lock, pr)
     orc = oracle.Oracle(shape, W, run, lock, prompts)
     B, N = run.batch, run.seq_len
-    rep = dict(steps=0, replays=0, frozen_steps=0, max_frozen=0, returns=0, cycles=0)
+    rep = dict(steps=0, replays=0, frozen_steps=0, max_frozen=0, returns=0, cycles=0,
+               argmax_near_tie=0, ambiguous=0)
     returned = np.zeros((B, N), bool)  # unfrozen by the last update
     for t in range(run.steps):
         m = eng.step()
         orc.step()
         torch.cuda.synchronize()
-        seq_o, pos_o, _ = orc.rows()
+        seq_o, pos_o, real_o = orc.rows()
         rs, rp, _ = (a.cpu().numpy() for a in eng.rows())
         assert m == orc.m and np.array_equal(rs, seq_o) and np.array_equal(rp, pos_o), \
             f"step {t}: active rows"
@@ -186,14 +234,27 @@ def run_slowfast_lockstep(shape, W, run, lock, prompts):
         assert dz.max() <= logit_tol(shape, scale), f"step {t}: logits {dz.max():.3g}"
         so = orc.stats()
         sg = {k: v.cpu().numpy() for k, v in eng.stats().items()}
+        near_tie = top2_gap(zo, shape.mask_id) <= np.maximum(2.0 * dz.max(axis=1),
+                                                              1e-6 * max(scale, 1.0))
+        am_bad = sg["argmax"] != so["argmax"]
+        assert not (am_bad & ~near_tie).any(), f"step {t}: argmax differs outside a near tie"
+        rep["argmax_near_tie"] += int(am_bad.sum())
+        dconf_all = np.abs(sg["conf"] - so["conf"])
+        assert (dconf_all <= 1e-5 + 2.0 * so["conf"] * (5e-3 if shape.bf16 else 1e-4)).all(), \
+            f"step {t}: conf"
         assert np.array_equal(sg["has_kl"].astype(np.uint8), so["has_kl"]), f"step {t}: has_kl"
+        hk = so["has_kl"].astype(bool)
+        if hk.any():
+            dkl = np.abs(sg["kl"][hk] - so["kl"][hk])
+            kl_tol = (2e-6 + 1e-3 * np.abs(so["kl"][hk])) if not shape.bf16 else (
+                1e-4 + 5e-2 * np.abs(so["kl"][hk]))
+            assert (dkl <= kl_tol).all(), f"step {t}: KL"
         back = returned[seq_o, pos_o]
         assert not so["has_kl"][back].any(), f"step {t}: KL on a position back from frozen"
         rep["returns"] += int(back.sum())
-        dconf = float(np.abs(sg["conf"] - so["conf"]).max())
-        margin = _sf_margin(orc, lock, shape, so)
-        st0 = orc.sf_state()[:, 0].copy()
-        frozen_before = orc.frozen().astype(bool)
+        dconf = float(dconf_all.max())
+        pre = dict(x=orc.tokens(), frozen=orc.frozen(), has_prev=orc.has_prev(),
+                   state=orc.sf_state())
         orc.lock_update()
         eng.lock_update()
         torch.cuda.synchronize()
@@ -205,9 +266,35 @@ def run_slowfast_lockstep(shape, W, run, lock, prompts):
                    state=eng.sf_state().cpu().numpy()[:, :13],
                    has_prev=eng.has_prev().cpu().numpy().astype(np.uint8))
         diff = [k for k in want if not np.array_equal(got[k], want[k].reshape(got[k].shape))]
+        # the oracle's decision margin at this step (every step, so that the
+        # number of ambiguous steps bounds the replays)
+        margin = min(_sf_decision_margin(run, lock, shape.mask_id, pos_o[seq_o == b],
+                                         so["conf"][seq_o == b], pre["x"][b],
+                                         pre["state"][b], want["state"][b]) for b in range(B))
+        ambiguous = margin <= 2.0 * dconf + 1e-12
+        rep["ambiguous"] += int(ambiguous)
         if diff:
-            assert margin <= 2.0 * dconf + 1e-12, \
-                f"step {t}: {diff} differ with decision margin {margin:.3g} > 2 x {dconf:.3g}"
+            # (a) the engine followed the rule on its own statistics
+            rx, rf, rh, rst = _rule_on(run, lock, shape.mask_id, rs, rp,
+                                       sg["argmax"].astype(np.int32),
+                                       sg["conf"].astype(np.float64), pre["x"], pre["frozen"],
+                                       pre["has_prev"], pre["state"])
+            assert np.array_equal(rx, got["tokens"]) and np.array_equal(rf, got["frozen"]) and \
+                np.array_equal(rh, got["has_prev"]) and np.array_equal(rst, got["state"]), \
+                f"step {t}: the engine's decision is not the rule on its own statistics"
+            # (b) the oracle's decision sits within the confidence error of a
+            # comparison the rule made
+            if any(k != "locks" for k in diff):
+                assert ambiguous, \
+                    f"step {t}: {diff} differ with decision margin {margin:.3g} > 2 x {dconf:.3g}"
+            for b, p in np.argwhere(got["locks"] != want["locks"]):
+                i = np.nonzero((seq_o == b) & (pos_o == p))[0]
+                assert len(i) == 1 and real_o[i[0]] and so["has_kl"][i[0]], \
+                    f"step {t}: lock state differs at ({b},{p}) where no test applies"
+                i = i[0]
+                assert abs(so["kl"][i] - lock["kl_eps"]) < MARGIN or \
+                    abs(so["conf"][i] - lock["conf_tau"]) < MARGIN, \
+                    f"step {t}: lock decision differs at ({b},{p}) outside the margin"
             eng.tokens().copy_(torch.from_numpy(want["tokens"]).to(DEV))
             eng.lock_bits().copy_(torch.from_numpy(
                 synth_bits(want["locks"]).view(np.int64)).to(DEV))
@@ -220,10 +307,10 @@ def run_slowfast_lockstep(shape, W, run, lock, prompts):
             torch.cuda.synchronize()
             rep["replays"] += 1
         rep["steps"] += 1
-        rep["cycles"] += int(((st0 == 1) & (want["state"][:, 0] == 0)).sum())
+        rep["cycles"] += int(((pre["state"][:, 0] == 1) & (want["state"][:, 0] == 0)).sum())
         rep["frozen_steps"] += int(want["frozen"].any())
         rep["max_frozen"] = max(rep["max_frozen"], int(want["frozen"].sum()))
-        returned = frozen_before & ~want["frozen"].astype(bool)
+        returned = pre["frozen"].astype(bool) & ~want["frozen"].astype(bool)
     eng.close()
     return rep
 
@@ -242,8 +329,9 @@ def test_slowfast_lockstep_tiny_fp32(tiny_case):
     lock, e = _engineered_lock(W, shape, TINY_SF_RUN, pr, sf_k=2, sf_kmax=4)
     rep = run_slowfast_lockstep(shape, W, TINY_SF_RUN, lock, pr)
     print(f"\n[slowfast tiny fp32] end point {e} {rep}")
+    append_record(dict(name="slowfast/tiny-fp32", **rep))
     assert rep["frozen_steps"] > 0 and rep["returns"] > 0 and rep["cycles"] > 0
-    assert rep["replays"] <= rep["steps"] // 4
+    assert rep["replays"] <= min(rep["ambiguous"], rep["steps"] // 4), rep
 
 
 def test_slowfast_lockstep_bf16_two_sequences():
@@ -254,7 +342,13 @@ def test_slowfast_lockstep_bf16_two_sequences():
     lock, e = _engineered_lock(W, shape, run, pr, sf_k=3, sf_kmax=6)
     rep = run_slowfast_lockstep(shape, W, run, lock, pr)
     print(f"\n[slowfast bf16] end point {e} {rep}")
+    append_record(dict(name="slowfast/bf16-two-sequences", **rep))
     assert rep["cycles"] > 0
+    # random weights: the masked positions share one input embedding, so
+    # their confidences nearly coincide and the ranking the rule takes is
+    # within the bf16 confidence error at most steps; a replay happens only
+    # at such an ambiguous step (asserted per step above)
+    assert rep["replays"] <= rep["ambiguous"], rep
 
 
 def test_slowfast_llada_full_shape_invariants():

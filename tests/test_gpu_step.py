@@ -110,14 +110,23 @@ def test_empty_active_set_and_forced_locks(tiny):
 
 def test_nan_weight_is_latched_and_reported(tiny):
     """A NaN in the LM head makes the log-normaliser non-finite; the device
-    latches it and the next dlm_step returns DLM_E_NUMERIC."""
+    latches it, the lock update commits and locks nothing from that step, and
+    the next dlm_step returns DLM_E_NUMERIC."""
     shape, run, W, pr = tiny
     dev = torch.device("cuda")
     dw = E.upload_weights(W, shape, dev)
     dw["lm_head"][3, 5] = float("nan")
-    eng = E.Engine(shape, dw, run, synth.LOCK_SETTINGS["natural"], torch.from_numpy(pr).to(dev))
+    eng = E.Engine(shape, dw, run, synth.LOCK_SETTINGS["scheduled"],
+                   torch.from_numpy(pr).to(dev))
     eng.step()
+    tok0 = eng.tokens().cpu().numpy().copy()
+    bits0 = eng.lock_bits().cpu().numpy().copy()
+    cnt0 = eng.counters().cpu().numpy().copy()
     eng.lock_update()
+    torch.cuda.synchronize()
+    assert np.array_equal(eng.tokens().cpu().numpy(), tok0)
+    assert np.array_equal(eng.lock_bits().cpu().numpy(), bits0)
+    assert np.array_equal(eng.counters().cpu().numpy(), cnt0)
     from selective_token_recompute_amd._lib import DLM_E_NUMERIC, DlmError
     with pytest.raises(DlmError) as ei:
         eng.step()
