@@ -67,6 +67,26 @@ int dlm_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, con
                 const int32_t* row_pos, int32_t seq_len, int32_t mask_id, void* ws,
                 size_t ws_bytes, void* stream);
 
+/* dlm_op_gemm without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and launch
+ * plan as dlm_op_gemm given dlm_op_gemm_ws_bytes() of workspace; the split-K
+ * partial sums go to a file-scope device array of
+ * dlm_op_gemm_noalloc_max_bytes() bytes (8 MiB) that each GPU the library
+ * runs on holds until the process ends.  The call allocates nothing.
+ * Returns DLM_E_SIZE, before any launch, when the plan's partials
+ * (dlm_op_gemm_ws_bytes(dtype, epi, M, N, K)) exceed that size.  Every call
+ * on one GPU shares that GPU's array and the partials need no initial
+ * contents (each split writes all of its own); calls that overlap on one
+ * GPU (different streams, or threads) race on it and must be serialised by
+ * the caller.  The stream (NULL: the current device's null stream) selects
+ * the GPU. */
+size_t dlm_op_gemm_noalloc_max_bytes(void);
+int dlm_op_gemm_noalloc(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K,
+                        const void* A, const void* W, const void* W2, void* C,
+                        const int32_t* row_seq, const int32_t* row_pos, int32_t seq_len,
+                        int32_t mask_id, void* stream);
+
 /* The same GEMM with a forced launch configuration, for tuning and for
  * testing every configuration the plan can choose: cfg indexes the bf16 MFMA
  * tile table (dlm_op_gemm_num_configs() entries; < 0 = the default plan),

@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -251,6 +252,47 @@ hipError_t timed(dlm_handle* h, int cls, double bytes, double flops, F&& launch)
     if (_e != hipSuccess) return DLM_E_HIP; \
   } while (0)
 
+}  // namespace
+
+// Workspace of dlm_op_gemm_noalloc: split-K partial sums in a file-scope
+// device array, so that the call needs no allocation (one copy per GPU the
+// library runs on, held until the process ends).  Host code never uses the
+// array's name as an address: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+namespace {
+constexpr size_t kGemmScratchBytes = size_t(8) << 20;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kGemmScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the device that owns `stream` (the
+// current device for the null stream).
+int gemm_scratch_for(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return DLM_E_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = 0;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return DLM_E_HIP;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return DLM_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return DLM_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return DLM_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DLM_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -698,6 +740,29 @@ int dlm_op_gemm(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, con
 }
 
 int dlm_op_gemm_num_configs(void) { return gemm_num_configs(); }
+
+size_t dlm_op_gemm_noalloc_max_bytes(void) { return kGemmScratchBytes; }
+
+int dlm_op_gemm_noalloc(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K,
+                        const void* A, const void* W, const void* W2, void* C,
+                        const int32_t* row_seq, const int32_t* row_pos, int32_t seq_len,
+                        int32_t mask_id, void* stream) {
+  if (!dt_ok(dtype) || epi < 0 || epi > 3 || M < 0 || N < 1 || K < 1) return DLM_E_INVALID;
+  if (M == 0) return DLM_OK;
+  if (!A || !W || !C || (epi == kEpiSwiglu && !W2)) return DLM_E_INVALID;
+  if (epi == kEpiLogits && (!row_seq || !row_pos || seq_len < 1)) return DLM_E_INVALID;
+  auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (!al16(A) || !al16(W) || (W2 && !al16(W2))) return DLM_E_INVALID;
+  // the plan dlm_op_gemm takes with enough workspace; its split-K partials
+  // must fit the scratch array
+  if (gemm_ws_bytes(dtype, epi, M, N, K) > kGemmScratchBytes) return DLM_E_SIZE;
+  void* ws = nullptr;
+  const int st = gemm_scratch_for((hipStream_t)stream, &ws);
+  if (st != DLM_OK) return st;
+  GemmArgs g{dtype, epi, M, N, K, A, W, W2, C, row_seq, row_pos, seq_len, mask_id,
+             nullptr, nullptr, nullptr, nullptr, 0, 0};
+  return hip_status(launch_gemm(g, ws, kGemmScratchBytes, (hipStream_t)stream));
+}
 
 int dlm_op_gemm_config(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K,
                        const void* A, const void* W, const void* W2, void* C,

@@ -82,6 +82,22 @@ def gemm(epi: int, A: torch.Tensor, W: torch.Tensor, W2=None, C=None, row_seq=No
     return C
 
 
+def gemm_noalloc_max_bytes() -> int:
+    return int(L.lib().dlm_op_gemm_noalloc_max_bytes())
+
+
+def gemm_noalloc(epi: int, A: torch.Tensor, W: torch.Tensor, C: torch.Tensor, W2=None,
+                 row_seq=None, row_pos=None, seq_len: int = 0, mask_id: int = 0) -> torch.Tensor:
+    """dlm_op_gemm_noalloc: the GEMM with its split-K partials in the
+    library's device scratch array; C must be given (nothing is allocated)."""
+    M, K = A.shape
+    N = W.shape[0]
+    L.check(L.lib().dlm_op_gemm_noalloc(_dt(A), epi, M, N, K, _p(A), _p(W), _p(W2), _p(C),
+                                        _p(row_seq), _p(row_pos), seq_len, mask_id, _s()),
+            "dlm_op_gemm_noalloc")
+    return C
+
+
 def gemm_config(epi: int, A, W, cfg: int, splits: int = 0, W2=None, C=None, row_seq=None,
                 row_pos=None, seq_len: int = 0, mask_id: int = 0):
     """GEMM with a forced tile configuration (cfg) and split-K factor."""
