@@ -151,6 +151,25 @@ int dlm_op_attention_config(int32_t dtype, int32_t M, int32_t batch, int32_t seq
                             int32_t stages, int32_t key_halves, int32_t qblocks,
                             int32_t key_tile, void* ws, size_t ws_bytes, void* stream);
 
+/* The same attention on the 32x32-MFMA kernel (bf16, head_dim 64 or 128,
+ * seq_len a multiple of the layout's key tile; else DLM_E_UNSUPPORTED) with
+ * a forced wave layout and key split, for tuning sweeps and for testing
+ * every layout the plan may choose.  layout indexes the kernel's layout
+ * table (dlm_op_attention_num_layouts() entries: keys per LDS tile, ring
+ * depth, query waves, key groups, 32-query blocks per wave; -1: the plan's
+ * layout); splits > 0 forces that many key ranges (clamped to the number of
+ * key tiles; partial results merged by log-sum-exp in a second pass), 0 the
+ * plan's count.  ws must hold dlm_op_attention_layout_ws_bytes() bytes;
+ * DLM_E_SIZE otherwise. */
+int dlm_op_attention_num_layouts(void);
+size_t dlm_op_attention_layout_ws_bytes(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len,
+                                        int32_t nq, int32_t nkv, int32_t hd, int32_t splits,
+                                        int32_t layout);
+int dlm_op_attention_layout(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, int32_t nq,
+                            int32_t nkv, int32_t hd, const void* q, const int32_t* row_start,
+                            const void* kcache, const void* vcache, void* o, int32_t splits,
+                            int32_t layout, void* ws, size_t ws_bytes, void* stream);
+
 /* QKV projection with the rotary embedding and the K/V cache scatter in the
  * GEMM epilogue (SureLock page, §2: fresh Q/K/V only for the active rows,
  * K/V of every position kept in the cache), as dlm_step runs it for bf16

@@ -37,7 +37,8 @@ EXPORTS = [
     "dlm_op_attention_config", "dlm_op_vocab_ws_bytes",
     "dlm_op_vocab_stats", "dlm_op_lm_head_stats_ws_bytes", "dlm_op_lm_head_stats",
     "dlm_op_commit_lock", "dlm_op_slowfast_commit", "dlm_op_gemm_noalloc_max_bytes",
-    "dlm_op_gemm_noalloc",
+    "dlm_op_gemm_noalloc", "dlm_op_attention_num_layouts", "dlm_op_attention_layout_ws_bytes",
+    "dlm_op_attention_layout",
 ]
 
 i32 = ctypes.c_int32
@@ -113,6 +114,9 @@ def lib() -> ctypes.CDLL:
         L.dlm_op_gemm_ws_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.dlm_op_gemm.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp,
                                   sz, vp]
+        L.dlm_op_attention_layout_ws_bytes.restype = sz
+        L.dlm_op_attention_layout_ws_bytes.argtypes = [i32] * 9
+        L.dlm_op_attention_layout.argtypes = [i32] * 7 + [vp] * 5 + [i32, i32, vp, sz, vp]
         L.dlm_op_gemm_noalloc_max_bytes.restype = sz
         L.dlm_op_gemm_noalloc_max_bytes.argtypes = []
         L.dlm_op_gemm_noalloc.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32,

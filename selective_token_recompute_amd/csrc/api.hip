@@ -870,6 +870,41 @@ int dlm_op_attention_config(int32_t dtype, int32_t M, int32_t batch, int32_t seq
                                          key_halves, qblocks, key_tile, (hipStream_t)stream));
 }
 
+int dlm_op_attention_num_layouts(void) { return attention_num_layouts(); }
+
+size_t dlm_op_attention_layout_ws_bytes(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len,
+                                        int32_t nq, int32_t nkv, int32_t hd, int32_t splits,
+                                        int32_t layout) {
+  if (!dt_ok(dtype) || M < 0 || batch < 1 || seq_len < 1 || nq < 1 || nkv < 1 || nq % nkv ||
+      splits < 0)
+    return 0;
+  return attention_layout_ws_bytes(dtype, M, batch, seq_len, nq, nkv, hd, splits, layout);
+}
+
+int dlm_op_attention_layout(int32_t dtype, int32_t M, int32_t batch, int32_t seq_len, int32_t nq,
+                            int32_t nkv, int32_t hd, const void* q, const int32_t* row_start,
+                            const void* kcache, const void* vcache, void* o, int32_t splits,
+                            int32_t layout, void* ws, size_t ws_bytes, void* stream) {
+  if (!dt_ok(dtype) || M < 0 || batch < 1 || seq_len < 1 || nq < 1 || nkv < 1 || nq % nkv ||
+      splits < 0 || layout < -1 || layout >= attention_num_layouts())
+    return DLM_E_INVALID;
+  if (M == 0) return DLM_OK;
+  if (!q || !row_start || !kcache || !vcache || !o) return DLM_E_INVALID;
+  if (layout >= 0 && !attention_layout_supported(dtype, seq_len, hd, layout))
+    return DLM_E_UNSUPPORTED;
+  if (layout < 0 && attention_layout_ws_bytes(dtype, M, batch, seq_len, nq, nkv, hd, 0, -1) == 0 &&
+      !(dtype == DLM_BF16 && (hd == 64 || hd == 128) && seq_len % 64 == 0))
+    return DLM_E_UNSUPPORTED;
+  if (attention_layout_ws_bytes(dtype, M, batch, seq_len, nq, nkv, hd, splits, layout) >
+      (ws ? ws_bytes : 0))
+    return DLM_E_SIZE;
+  const hipError_t e = launch_attention_layout(dtype, M, batch, seq_len, nq, nkv, hd, q,
+                                               row_start, kcache, vcache, o, ws,
+                                               ws ? ws_bytes : 0, splits, layout,
+                                               (hipStream_t)stream);
+  return e == hipErrorInvalidValue ? DLM_E_UNSUPPORTED : hip_status(e);
+}
+
 size_t dlm_op_vocab_ws_bytes(int32_t M, int32_t V) {
   if (M < 0 || V < 1) return 0;
   return vocab_ws_bytes(M, V);

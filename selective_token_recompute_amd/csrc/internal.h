@@ -112,6 +112,18 @@ hipError_t launch_attention_cfg(int dtype, int M, int B, int N, int nq, int nkv,
                                 int stages, int key_halves, int qblocks, int key_tile,
                                 hipStream_t s);
 
+// 32x32 MFMA attention with a forced layout (index into its layout table)
+// and split count (0: the plan's); false / invalid when the layout does not
+// apply (dtype, head dim, N not a multiple of its key tile).
+int attention_num_layouts();
+bool attention_layout_supported(int dtype, int N, int hd, int layout);
+size_t attention_layout_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd,
+                                 int splits, int layout);
+hipError_t launch_attention_layout(int dtype, int M, int B, int N, int nq, int nkv, int hd,
+                                   const void* q, const int32_t* row_start, const void* kc,
+                                   const void* vc, void* o, void* ws, size_t ws_bytes, int splits,
+                                   int layout, hipStream_t s);
+
 // ---- vocabulary statistics ----------------------------------------------------------
 size_t vocab_ws_bytes(int M, int V);
 hipError_t launch_vocab_stats(int M, int V, int mask_id, int kl_dir, int N,

@@ -549,6 +549,332 @@ __global__ __launch_bounds__(64 * (4 / QB) * KH) void attn_mfma_dma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// 32x32 MFMA kernel (bf16, hd 64 or 128; N a multiple of the key tile KT).
+//
+// A workgroup owns QT = QW * QB * 32 query vectors of one (sequence, kv head)
+// and one key range, and streams the range's K and V^T tiles through an
+// STAGES-deep LDS ring with direct global->LDS loads.  Wave (qw, kh) holds
+// QB blocks of 32 query vectors and takes keys [kh KT/KH, (kh+1) KT/KH) of
+// every tile, in 32-key blocks:
+//   S^T (32 keys x 32 queries) = K Q^T with v_mfma_f32_32x32x16_bf16, Q^T
+//     from registers (lane l: query l%32, head dims 16c + 8(l/32) .. +7);
+//     lane l supplies K row pi(l%32) of the block, where pi swaps bits 2 and
+//     3 of the row index, so that accumulator register 8s + e of lane l
+//     holds key 16s + 8(l/32) + e of the block for query l%32;
+//   O^T (hd x 32 queries) += V^T P^T with the same MFMA: registers 8s..8s+7
+//     of S^T, exponentiated and rounded to bf16, are exactly the B operand of
+//     key step s, and the A operand is 8 consecutive keys of one V^T row (one
+//     16-byte LDS read).
+// One K/V fragment read from LDS thus feeds 32 queries (64 with QB = 2), and
+// P never leaves registers.  Online softmax per query in base 2 with a lazily
+// raised maximum; the two lanes l and l^32 of a query combine by
+// permlane32_swap.  The KH key groups of a query block merge through LDS at
+// the end; split-KV (gridDim.z > 1) writes unnormalised partials for the
+// combine pass.
+__device__ __forceinline__ int pi32(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+// 16-byte slot XOR of a K row (HD * 2 bytes) or V^T row (KT * 2 bytes): the
+// rows one 8-lane group of a fragment read touches land on distinct slots
+// (16-slot rows: r & 15; 8-slot rows: rows {0-3, 8-11} and {4-7, 12-15}
+// are the groups, hence bit 3 moves to bit 2)
+template <int CH>
+__device__ __forceinline__ int a32_swz(int r) {
+  if constexpr (CH == 16) return r & 15;
+  else return (r & 3) | ((r >> 1) & 4);
+}
+// V^T rows: the 8 lanes of a group read 8 consecutive rows at one chunk
+template <int CH>
+__device__ __forceinline__ int a32_vswz(int r) {
+  return CH == 16 ? (r & 15) : (r & 7);
+}
+
+template <int HD, int QB>
+constexpr size_t attn32_merge_bytes(int KH, int QW) {
+  return KH == 1 ? 0 : (size_t)(KH / 2) * QW * QB * ((HD / 32) * 16 * 64 * 4 + 64 * 8);
+}
+
+template <int HD, int KT, int STAGES, int QW, int KH, int QB, bool SPLIT>
+__global__ __launch_bounds__(64 * QW * KH, 1) void attn32_kernel(
+    const bf16_t* __restrict__ q, const int32_t* __restrict__ row_start,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, bf16_t* __restrict__ o, int N,
+    int nq, int nkv, int keys_per_split, int M, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  static_assert(HD == 64 || HD == 128, "head dim");
+  static_assert(KT == 64 || KT == 128, "key tile");
+  static_assert(QB == 1 || QB == 2, "query blocks per wave");
+  constexpr int NWV = QW * KH;
+  constexpr int QT = QW * QB * 32;       // query vectors per workgroup
+  constexpr int KW = KT / KH;            // keys per wave per tile
+  static_assert(KW % 32 == 0, "a wave takes whole 32-key blocks");
+  constexpr int KB = KW / 32;
+  constexpr int NKC = HD / 16;           // k-steps of S (head dims)
+  constexpr int NHB = HD / 32;           // 32-row blocks of O^T
+  constexpr int KRB = HD * 2, KCH = KRB / 16;  // K row bytes, 16-byte chunks per row
+  constexpr int VRB = KT * 2, VCH = VRB / 16;  // V^T row bytes in a tile, chunks per row
+  constexpr int K_BYTES = KT * KRB, V_BYTES = HD * VRB, STAGE = K_BYTES + V_BYTES;
+  constexpr int K_INSTR = K_BYTES / 1024, V_INSTR = V_BYTES / 1024;
+  constexpr int IPW = (K_INSTR + V_INSTR) / NWV;  // load instructions per wave per tile
+  static_assert((K_INSTR + V_INSTR) % NWV == 0, "instructions per wave");
+  static_assert((STAGES - 1) * IPW < 64, "in-flight loads must fit the vmcnt counter");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qw = wave % QW, kh = wave / QW;
+  const int g = lane >> 5, l32 = lane & 31;
+  // XCD-aware order (workgroup i runs on XCD i % 8): consecutive workgroups
+  // of one XCD take the query tiles and key ranges of one (sequence, kv
+  // head), whose K/V then stream through that XCD's L2
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int total = nx * ny * gridDim.z;
+  int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  const int bx = lin % nx, by = (lin / nx) % ny, bz = lin / (nx * ny);
+  const int b = by / nkv, gk = by % nkv;
+  const int G = nq / nkv;
+  const int r0 = row_start[b], Qn = (row_start[b + 1] - r0) * G;
+  const int qbase = bx * QT;
+  if (qbase >= Qn) return;  // uniform over the workgroup
+
+  bool qok[QB];
+  int row[QB], head[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qv = qbase + (qw * QB + qb) * 32 + l32;
+    qok[qb] = qv < Qn;
+    row[qb] = r0 + (qok[qb] ? qv / G : 0);
+    head[qb] = gk * G + (qok[qb] ? qv % G : 0);
+  }
+  const bool wave_live = qbase + qw * QB * 32 < Qn;  // wave-uniform
+  const size_t slab = ((size_t)b * nkv + gk) * N * HD;
+  const bf16_t* kslab = kc + slab;  // [N][HD]
+  const bf16_t* vslab = vc + slab;  // [HD][N]
+  const int key0 = bz * keys_per_split;
+  const int key1 = min(N, key0 + keys_per_split);
+  const int ntiles = key1 > key0 ? (key1 - key0) / KT : 0;
+  const float scale = kLog2e / sqrtf((float)HD);
+
+  // this lane's global source and LDS destination for each of its load
+  // instructions (tile 0): lane i of instruction j fills 16-byte slot i % CH
+  // of row j * (64 / CH) + i / CH, from the row's chunk slot ^ swizzle
+  const bf16_t* src[IPW];
+  int dst[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int j = wave + i * NWV;
+    if (j < K_INSTR) {
+      const int kr = j * (1024 / KRB) + lane / KCH;
+      const int lc = (lane % KCH) ^ a32_swz<KCH>(kr);
+      src[i] = kslab + (size_t)(key0 + kr) * HD + lc * 8;
+      dst[i] = j * 1024;
+    } else {
+      const int jv = j - K_INSTR;
+      const int vr = jv * (1024 / VRB) + lane / VCH;
+      const int lc = (lane % VCH) ^ a32_vswz<VCH>(vr);
+      src[i] = vslab + (size_t)vr * N + key0 + lc * 8;
+      dst[i] = K_BYTES + jv * 1024;
+    }
+  }
+  auto issue = [&](int t) {
+    unsigned char* st = smem + (t % STAGES) * STAGE;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int j = wave + i * NWV;
+      const size_t adv = j < K_INSTR ? (size_t)t * KT * HD : (size_t)t * KT;
+      attn_dma16(src[i] + adv, st + dst[i]);
+    }
+  };
+
+  float m_run[QB], l_run[QB];
+  f32x16 oacc[QB][NHB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][hb][r] = 0.f;
+  }
+
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < ntiles) issue(t);
+  // query fragments (B operand of S^T) while the first tiles are in flight
+  bf16x8 qf[QB][NKC];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bf16_t* qp = q + (size_t)row[qb] * nq * HD + (size_t)head[qb] * HD + g * 8;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      if (qok[qb]) {
+        qf[qb][c] = *(const bf16x8*)(qp + c * 16);
+      } else {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        qf[qb][c] = *(const bf16x8*)&z;
+      }
+    }
+  }
+
+  const int kofs = kh * KW;  // this wave's first key in a tile
+  for (int t = 0; t < ntiles; ++t) {
+    attn_wait_tiles<IPW, STAGES - 1>(min(STAGES - 2, ntiles - 1 - t));
+    attn_lds_barrier();
+    if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1);
+    if (!wave_live) continue;  // no valid query in this wave: loads only
+    const unsigned char* st = smem + (t % STAGES) * STAGE;
+    f32x16 s[QB][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+      const int kr = kofs + kb * 32 + pi32(l32);
+      const unsigned char* krow = st + kr * KRB;
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+        const bf16x8 a = *(const bf16x8*)(krow + (((2 * c + g) ^ a32_swz<KCH>(kr)) << 4));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][c], s[qb][kb], 0, 0, 0);
+      }
+    }
+    bf16x8 pb[QB][KB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+      mx = xor32_max(mx) * scale;
+      if (__any(mx > m_run[qb] + kLazyMax)) {  // wave-uniform branch
+        const float m_new = fmaxf(m_run[qb], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);  // -inf -> 0
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) oacc[qb][hb] *= alpha;
+        m_run[qb] = m_new;
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][8 * sb + e], scale, -m_run[qb]));
+            psum += p[e];
+          }
+          const uint4 w = make_uint4(f2bf2(p[0], p[1]), f2bf2(p[2], p[3]), f2bf2(p[4], p[5]),
+                                     f2bf2(p[6], p[7]));
+          pb[qb][kb][sb] = __builtin_bit_cast(bf16x8, w);
+        }
+      l_run[qb] += xor32_sum(psum);
+    }
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int vr = hb * 32 + l32;
+      const unsigned char* vrow = st + K_BYTES + vr * VRB;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int ch = (kofs + kb * 32 + sb * 16) / 8 + g;
+          const bf16x8 va = *(const bf16x8*)(vrow + ((ch ^ a32_vswz<VCH>(vr)) << 4));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][hb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb][kb][sb], oacc[qb][hb], 0, 0, 0);
+        }
+    }
+  }
+
+  if constexpr (KH > 1) {
+    // merge the key groups in pairs by the log-sum-exp rule: in the round of
+    // width h, groups [h, 2h) hand their state to groups [0, h) through LDS;
+    // every wave takes part in every barrier
+    constexpr int OB = NHB * 16 * 64 * 4;          // O^T registers of one query block
+    constexpr int REG = QB * (OB + 64 * 8);       // + (m, l) per lane
+    attn_lds_barrier();  // every wave is done with the tiles in LDS
+#pragma unroll
+    for (int h = KH / 2; h >= 1; h /= 2) {
+      if (kh >= h && kh < 2 * h) {
+        unsigned char* mine = smem + ((kh - h) * QW + qw) * REG;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              ((f32x4*)(mine + qb * OB))[(hb * 4 + r4) * 64 + lane] =
+                  f32x4{oacc[qb][hb][4 * r4], oacc[qb][hb][4 * r4 + 1], oacc[qb][hb][4 * r4 + 2],
+                        oacc[qb][hb][4 * r4 + 3]};
+          ((float2*)(mine + QB * OB))[qb * 64 + lane] = make_float2(m_run[qb], l_run[qb]);
+        }
+      }
+      attn_lds_barrier();
+      if (kh < h) {
+        const unsigned char* other = smem + (kh * QW + qw) * REG;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float2 ml = ((const float2*)(other + QB * OB))[qb * 64 + lane];
+          const float m = fmaxf(m_run[qb], ml.x);
+          const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m);
+          const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - m);
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 v = ((const f32x4*)(other + qb * OB))[(hb * 4 + r4) * 64 + lane];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                oacc[qb][hb][4 * r4 + e] = oacc[qb][hb][4 * r4 + e] * a0 + v[e] * a1;
+            }
+          l_run[qb] = l_run[qb] * a0 + ml.y * a1;
+          m_run[qb] = m;
+        }
+      }
+      attn_lds_barrier();  // the slots are read before the next round writes
+    }
+    if (kh != 0) return;
+  }
+
+  // lane l holds query l%32 and head dims 32 hb + 8 i + 4 (l/32) + j in
+  // register 4 i + j of block hb
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (!qok[qb]) continue;
+    const int gq = row[qb] * nq + head[qb];
+    if (SPLIT) {
+      const size_t base = (size_t)bz * M * nq + gq;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(f32x4*)(part_o + base * HD + hb * 32 + 8 * i + 4 * g) =
+              f32x4{oacc[qb][hb][4 * i], oacc[qb][hb][4 * i + 1], oacc[qb][hb][4 * i + 2],
+                    oacc[qb][hb][4 * i + 3]};
+      if (g == 0) *(float2*)(part_ml + base * 2) = make_float2(m_run[qb], l_run[qb]);
+    } else {
+      const float inv = 1.f / l_run[qb];
+      bf16_t* op = o + (size_t)row[qb] * nq * HD + (size_t)head[qb] * HD;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint2 w = make_uint2(f2bf2(oacc[qb][hb][4 * i] * inv, oacc[qb][hb][4 * i + 1] * inv),
+                                     f2bf2(oacc[qb][hb][4 * i + 2] * inv,
+                                           oacc[qb][hb][4 * i + 3] * inv));
+          *(uint2*)(op + hb * 32 + 8 * i + 4 * g) = w;
+        }
+    }
+  }
+}
+
 // Combine split-KV partials: o = sum_s o_s 2^(m_s - m) / sum_s l_s 2^(m_s - m),
 // m = max_s m_s; one thread per 4 consecutive output columns.
 template <typename T>
@@ -788,9 +1114,173 @@ hipError_t run_attn_mfma(const AttnPlan& p, int M, int B, int N, int nq, int nkv
   return hipGetLastError();
 }
 
+// ---- 32x32 MFMA kernel: layouts, plan, launch ---------------------------------
+
+struct A32Layout {
+  int kt, stages, qw, kh, qb;
+};
+// (keys per LDS tile, ring depth, query waves, key groups, 32-query blocks
+// per wave); query vectors per workgroup = 32 qw qb.  Kept from a sweep on
+// MI355X over one layer of 32 heads of 128 at N = 512 and 1024 and M = 9 ..
+// 1024 (kernels timed back to back in a HIP graph, 32 caches rotated);
+// dropped there: two query blocks per wave, one key group, 64-key tiles in
+// 3- to 5-deep rings, and a variant without LDS that loads each wave's K / V
+// fragments straight into registers (all slower at every point).
+constexpr A32Layout kA32[] = {
+    {128, 2, 1, 4, 1},  // 0: 32 queries, four key groups (4 waves)
+    {128, 2, 2, 4, 1},  // 1: 64 queries, four key groups (8 waves)
+    {128, 2, 4, 2, 1},  // 2: 128 queries, two key groups (8 waves)
+    {128, 2, 2, 2, 1},  // 3: 64 queries, two key groups (4 waves)
+};
+constexpr int kNumA32 = sizeof(kA32) / sizeof(kA32[0]);
+
+struct A32Plan {
+  bool ok;
+  int layout, qtiles, splits, keys_per_split;
+  size_t ws;
+};
+
+A32Plan make_a32_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd, int splits_in,
+                      int layout_in) {
+  A32Plan p{};
+  p.ok = dtype == kBF16 && (hd == 64 || hd == 128) && nq % nkv == 0 && M > 0;
+  if (!p.ok) return p;
+  const int G = nq / nkv;
+  int lay = layout_in;
+  // query vectors per (sequence, kv head), the rows spread evenly
+  const int qph = (M * G + B - 1) / B;
+  if (lay < 0 || lay >= kNumA32) {
+    // measured best: 128 queries per workgroup from ~768 per head, 64 from
+    // ~320, 32 between 64 and 320, and 64 below (one workgroup per head)
+    if (qph >= 768) lay = 2;
+    else if (qph >= 320) lay = 1;
+    else if (qph > 64) lay = 0;
+    else lay = 1;
+  }
+  const A32Layout& L = kA32[lay];
+  if (N % L.kt) {
+    p.ok = false;
+    return p;
+  }
+  p.layout = lay;
+  const int QT = 32 * L.qw * L.qb;
+  p.qtiles = (std::min(M, N) * G + QT - 1) / QT;
+  const int busy = std::max(1, (M * G + QT - 1) / QT) * nkv;
+  const int unit = L.kt;  // a key range is a whole number of LDS tiles
+  const int ktiles = N / unit;
+  auto ws_of = [&](int sp) { return (size_t)sp * M * nq * (hd + 2) * sizeof(float); };
+  int splits = 1;
+  if (splits_in > 0) {
+    splits = std::min(splits_in, ktiles);
+  } else {
+    // splitting the keys (partials merged by the combine pass) paid only
+    // from N = 1024, with few busy workgroups and at least two tiles per
+    // range: M = 20 (32 workgroups) 4 ranges, M = 102 (128) 2 ranges
+    while (N >= 1024 && busy * splits * 2 <= 256 && ktiles / (splits * 2) >= 2 &&
+           ws_of(splits * 2) <= kAttnSplitCap)
+      splits *= 2;
+  }
+  const int tiles_per = (ktiles + splits - 1) / splits;
+  p.splits = (ktiles + tiles_per - 1) / tiles_per;  // no empty key range
+  p.keys_per_split = tiles_per * unit;
+  p.ws = p.splits > 1 ? ws_of(p.splits) : 0;
+  return p;
+}
+
+template <int HD, int KT, int STAGES, int QW, int KH, int QB, bool SPLIT>
+void launch_a32(dim3 grid, const void* q, const int32_t* row_start, const void* kc,
+                const void* vc, void* o, int N, int nq, int nkv, int kps, int M, float* po,
+                float* pml, hipStream_t s) {
+  constexpr size_t ring = (size_t)STAGES * (KT * HD * 2 + HD * KT * 2);
+  constexpr size_t merge = attn32_merge_bytes<HD, QB>(KH, QW);
+  constexpr size_t lds = ring > merge ? ring : merge;
+  static_assert(lds <= 160 * 1024, "LDS of a CU");
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attn32_kernel<HD, KT, STAGES, QW, KH, QB, SPLIT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    attr = true;
+  }
+  attn32_kernel<HD, KT, STAGES, QW, KH, QB, SPLIT><<<grid, 64 * QW * KH, lds, s>>>(
+      (const bf16_t*)q, row_start, (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)o, N, nq, nkv,
+      kps, M, po, pml);
+}
+
+template <int HD, bool SPLIT>
+void launch_a32_layout(int lay, dim3 grid, const void* q, const int32_t* row_start,
+                       const void* kc, const void* vc, void* o, int N, int nq, int nkv, int kps,
+                       int M, float* po, float* pml, hipStream_t s) {
+#define DLM_A32(KT, ST, QW, KH, QB)                                                              \
+  launch_a32<HD, KT, ST, QW, KH, QB, SPLIT>(grid, q, row_start, kc, vc, o, N, nq, nkv, kps, M, \
+                                            po, pml, s)
+  switch (lay) {
+    case 0: DLM_A32(128, 2, 1, 4, 1); break;
+    case 1: DLM_A32(128, 2, 2, 4, 1); break;
+    case 2: DLM_A32(128, 2, 4, 2, 1); break;
+    default: DLM_A32(128, 2, 2, 2, 1); break;
+  }
+#undef DLM_A32
+}
+
+template <int HD>
+hipError_t run_a32(const A32Plan& p, int M, int B, int N, int nq, int nkv, const void* q,
+                   const int32_t* row_start, const void* kc, const void* vc, void* o, void* ws,
+                   hipStream_t s) {
+  dim3 grid(p.qtiles, B * nkv, p.splits);
+  if (p.splits > 1) {
+    float* po = (float*)ws;
+    float* pml = po + (size_t)p.splits * M * nq * HD;
+    launch_a32_layout<HD, true>(p.layout, grid, q, row_start, kc, vc, o, N, nq, nkv,
+                                p.keys_per_split, M, po, pml, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t total = (size_t)M * nq * (HD / 4);
+    const int gsz = (int)std::min<size_t>((total + 255) / 256, 8192);
+    attn_combine_kernel<bf16_t><<<gsz, 256, 0, s>>>(po, pml, p.splits, M * nq, HD, (bf16_t*)o);
+  } else {
+    launch_a32_layout<HD, false>(p.layout, grid, q, row_start, kc, vc, o, N, nq, nkv,
+                                 p.keys_per_split, M, nullptr, nullptr, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t run_a32_any(const A32Plan& p, int M, int B, int N, int nq, int nkv, int hd,
+                       const void* q, const int32_t* row_start, const void* kc, const void* vc,
+                       void* o, void* ws, hipStream_t s) {
+  if (hd == 128) return run_a32<128>(p, M, B, N, nq, nkv, q, row_start, kc, vc, o, ws, s);
+  return run_a32<64>(p, M, B, N, nq, nkv, q, row_start, kc, vc, o, ws, s);
+}
+
 }  // namespace
 
+int attention_num_layouts() { return kNumA32; }
+
+size_t attention_layout_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd,
+                                 int splits, int layout) {
+  const A32Plan p = make_a32_plan(dtype, M, B, N, nq, nkv, hd, splits, layout);
+  return p.ok ? p.ws : 0;
+}
+
+bool attention_layout_supported(int dtype, int N, int hd, int layout) {
+  if (dtype != kBF16 || (hd != 64 && hd != 128) || layout < 0 || layout >= kNumA32) return false;
+  return N % kA32[layout].kt == 0;
+}
+
+hipError_t launch_attention_layout(int dtype, int M, int B, int N, int nq, int nkv, int hd,
+                                   const void* q, const int32_t* row_start, const void* kc,
+                                   const void* vc, void* o, void* ws, size_t ws_bytes, int splits,
+                                   int layout, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  A32Plan p = make_a32_plan(dtype, M, B, N, nq, nkv, hd, splits, layout);
+  if (!p.ok) return hipErrorInvalidValue;
+  if (p.ws > ws_bytes) return hipErrorInvalidValue;
+  return run_a32_any(p, M, B, N, nq, nkv, hd, q, row_start, kc, vc, o, ws, s);
+}
+
 size_t attention_ws_bytes(int dtype, int M, int B, int N, int nq, int nkv, int hd) {
+  const A32Plan p = make_a32_plan(dtype, M, B, N, nq, nkv, hd, 0, -1);
+  if (p.ok) return p.ws;
   return make_attn_plan(dtype, M, B, N, nq, nkv, hd).ws;
 }
 
@@ -826,6 +1316,14 @@ hipError_t launch_attention_cfg(int dtype, int M, int B, int N, int nq, int nkv,
 hipError_t launch_attention(int dtype, int M, int B, int N, int nq, int nkv, int hd,
                             const void* q, const int32_t* row_start, const void* kc,
                             const void* vc, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  A32Plan p = make_a32_plan(dtype, M, B, N, nq, nkv, hd, 0, -1);
+  if (p.ok) {
+    if (p.ws > ws_bytes) {  // not enough workspace: one key range
+      p = make_a32_plan(dtype, M, B, N, nq, nkv, hd, 1, p.layout);
+    }
+    return run_a32_any(p, M, B, N, nq, nkv, hd, q, row_start, kc, vc, o, ws, s);
+  }
   return launch_attention_cfg(dtype, M, B, N, nq, nkv, hd, q, row_start, kc, vc, o, ws, ws_bytes,
                               0, 0, 0, 0, 0, s);
 }

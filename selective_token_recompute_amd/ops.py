@@ -189,6 +189,26 @@ def attention_config(q, row_start, kc, vc, nq, nkv, hd, splits=0, stages=0, key_
     return o
 
 
+def attention_num_layouts() -> int:
+    return int(L.lib().dlm_op_attention_num_layouts())
+
+
+def attention_layout(q, row_start, kc, vc, nq, nkv, hd, layout=-1, splits=0, o=None):
+    """attention() on the 32x32-MFMA kernel with a forced layout (-1: the
+    plan's) and split count (0: the plan's)."""
+    M = q.shape[0]
+    B, _, N, _ = kc.shape
+    dt = _dt(q)
+    if o is None:
+        o = torch.empty_like(q)
+    need = int(L.lib().dlm_op_attention_layout_ws_bytes(dt, M, B, N, nq, nkv, hd, splits, layout))
+    ws = _ws_cache(max(need, 256), q.device)
+    L.check(L.lib().dlm_op_attention_layout(dt, M, B, N, nq, nkv, hd, _p(q), _p(row_start),
+                                            _p(kc), _p(vc), _p(o), splits, layout, _p(ws),
+                                            ws.numel(), _s()), "dlm_op_attention_layout")
+    return o
+
+
 def vocab_stats(row_seq, row_pos, z_cur, z_prev, lse_prev, has_prev, lse_cur, mask_id,
                 kl_dir=0, ws=None):
     """z_cur/z_prev float [B][N][V]; has_prev int32 [B][N] (read, then set)."""

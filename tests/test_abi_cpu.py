@@ -161,4 +161,7 @@ def test_workspace_queries():
     assert L.lib().dlm_op_gemm_ws_bytes(1, 0, 1024, 12288, 4096) == 0
     assert L.lib().dlm_op_gemm_ws_bytes(0, 0, 8, 4096, 4096) == 0  # fp32 path: no split
     assert L.lib().dlm_op_vocab_ws_bytes(384, 126464) > 0
-    assert L.lib().dlm_op_attention_ws_bytes(1, 1, 1, 512, 32, 32, 128) > 0
+    # attention splits the keys (combine pass) only from N = 1024 at small M
+    assert L.lib().dlm_op_attention_ws_bytes(1, 20, 1, 1024, 32, 32, 128) > 0
+    assert L.lib().dlm_op_attention_ws_bytes(1, 1, 1, 512, 32, 32, 128) == 0
+    assert L.lib().dlm_op_attention_ws_bytes(1, 1024, 1, 1024, 32, 32, 128) == 0

@@ -21,7 +21,7 @@ import torch
 import oracle
 import synth
 from selective_token_recompute_amd import engine as E
-from tests.harness import append_record, bool_to_bits, logit_tol, top2_gap
+from tests.harness import append_record, bool_to_bits, conf_bound, logit_tol, top2_gap
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,9 @@ def _compare_rows(shape, eng, orc, sample, check_kl):
     bad = sg["argmax"][rows] != so["argmax"][rows]
     assert not (bad & ~near_tie).any()
     assert np.allclose(sg["lse"][rows], so["lse"][rows], rtol=0, atol=2e-2 * max(scale, 1.0))
-    assert (np.abs(sg["conf"][rows] - so["conf"][rows]) <= 1e-5 + 1e-2 * so["conf"][rows]).all()
+    dconf = np.abs(sg["conf"][rows] - so["conf"][rows])
+    assert (dconf <= conf_bound(so["conf"][rows], dz.max(axis=1))).all(), \
+        (dconf / so["conf"][rows]).max()
     kl_note = ""
     if check_kl:
         hk = so["has_kl"][rows].astype(bool)

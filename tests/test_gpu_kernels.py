@@ -211,6 +211,43 @@ def test_attention_wave_layouts(layout, key_tile, B, N, nq, nkv, hd, rows):
     assert (err <= 1e-2 + 2.0 ** -7 * np.abs(ref)).all(), err.max()
 
 
+@pytest.mark.parametrize("layout", list(range(ops.attention_num_layouts())))
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 64])
+@pytest.mark.parametrize("hd", [128, 64])
+def test_attention_32x32_layouts(layout, splits, hd):
+    """Every layout of the 32x32-MFMA kernel with each split count (the plan's,
+    none, two, a count that leaves a short last range, more than there are
+    key tiles), at both head sizes, with three sequences of ragged row counts
+    (one empty, one longer than a workgroup's query tile) and GQA, against
+    the oracle."""
+    B, N, nq, nkv = 3, 384, 8, 2
+    q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, [37, 0, 140], seed=17 + layout + hd)
+    o = ops.attention_layout(_dev(q.reshape(len(rs), nq * hd)), torch.from_numpy(rst).to(DEV),
+                             _dev(kc), _dev(vc.transpose(0, 1, 3, 2)), nq, nkv, hd,
+                             layout=layout, splits=splits)
+    ref = oracle.unit_attention(q, rs, kc, vc).reshape(len(rs), nq * hd)
+    err = np.abs(_f64(o) - ref)
+    assert (err <= 1e-2 + 2.0 ** -7 * np.abs(ref)).all(), err.max()
+
+
+@pytest.mark.parametrize("B,N,nq,nkv,rows", [
+    (1, 512, 32, 32, [384]),    # the LLaDA-8B step at M = 384
+    (1, 1024, 32, 32, [20]),    # one layer over a 1024-key cache at M = 20 (key splits)
+    (1, 512, 32, 32, [9]),      # the end of a scheduled-lock run
+    (2, 1024, 28, 4, [700, 1]),  # Dream-7B grouping, uneven sequences
+])
+def test_attention_32x32_default_plan(B, N, nq, nkv, rows):
+    """The default plan at the benchmark's shapes (layout and split count of
+    its own choosing), against the oracle."""
+    hd = 128
+    q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, rows, seed=N + nq + rows[0])
+    o = ops.attention(_dev(q.reshape(len(rs), nq * hd)), torch.from_numpy(rst).to(DEV),
+                      _dev(kc), _dev(vc.transpose(0, 1, 3, 2)), nq, nkv, hd)
+    ref = oracle.unit_attention(q, rs, kc, vc).reshape(len(rs), nq * hd)
+    err = np.abs(_f64(o) - ref)
+    assert (err <= 1e-2 + 2.0 ** -7 * np.abs(ref)).all(), err.max()
+
+
 def test_attention_fp32_generic():
     B, N, nq, nkv, hd = 2, 32, 4, 2, 16
     q, kc, vc, rs, rst = _attn_case(B, N, nq, nkv, hd, [20, 7], seed=3, bf16=False)
