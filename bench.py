@@ -40,11 +40,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_steps(eng_factory, K, timing=False):
+def run_steps(eng_factory, K, timing=False, flops_out=None):
     """K steps from the start of a run (new run every `steps` steps).
     Returns (seconds, decoded tokens, list of M, engine-timing dict or None);
     decoded tokens are counted from the engines' token arrays after the
-    timed region (positions past the prompt no longer holding the mask)."""
+    timed region (positions past the prompt no longer holding the mask).
+    flops_out (a list), if given, receives each step's algorithmic FLOPs as
+    the engine counts them (dlm_last_step_info)."""
     import torch
     acc = {}
 
@@ -69,6 +71,8 @@ def run_steps(eng_factory, K, timing=False):
             if timing:
                 eng.set_timing(True)
         ms.append(eng.step())
+        if flops_out is not None:
+            flops_out.append(eng.last_step_info()[2])
         eng.lock_update()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
@@ -157,40 +161,111 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     log(f"copy calibration: {reps} copies of {nbytes} bytes")
 
 
-def measured_ceilings():
-    """Ceilings measured on this GPU: a plain 1 GiB device-to-device copy
-    (read + write bytes over its event time) and this library's own bf16 GEMM
-    (default tile plan, plain fp32 store) on an 8192 x 8192 x 8192 problem."""
+def graph_timed(calls, reps=5):
+    """Seconds per call of a list of zero-argument launch functions, captured
+    once in a HIP graph (after one eager warm-up pass) and replayed reps
+    times, so that the host's launch overhead is not in the time; falls back
+    to eager launches between events when the capture fails."""
+    import torch
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for f in calls:
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+    except Exception:  # capture not supported by a call: eager launches
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            for f in calls:
+                f()
+        e1.record()
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / (reps * len(calls))
+
+
+# GEMM shapes of one LLaDA-8B step (N, K) and their epilogue in the engine
+STEP_GEMMS = {"gemm_qkv": (12288, 4096), "gemm_o": (4096, 4096), "gemm_gate_up": (12288, 4096),
+              "gemm_down": (4096, 12288), "gemm_lm_head": (126464, 4096)}
+
+
+def measured_ceilings(step_m=384):
+    """Ceilings measured on this GPU:
+    * a plain 1 GiB device-to-device copy (read + write bytes over its time);
+    * device copies moving 8.4 MB and 16.8 MB (one layer's K/V cache at
+      N = 512 and 1024), 32 buffers rotated, back to back in a HIP graph: the
+      bandwidth a kernel of that size reaches, launch and first DRAM round
+      trip included;
+    * hipBLASLt (torch.mm, bf16 in and out) on 8192 x 8192 x 8192, and this
+      library's GEMM (default plan, fp32 store) on the same problem;
+    * hipBLASLt against this library on each GEMM shape of the step at
+      M = step_m active rows (gate/up as one 2 d_ff-wide GEMM for hipBLASLt,
+      the SwiGLU epilogue here), both graph-timed."""
     import torch
     from selective_token_recompute_amd import ops, _lib as L
     n = 1 << 28
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-
-    def timed(f, reps):
-        f()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            f()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3 / reps
-
-    t_copy = timed(lambda: dst.copy_(src), 10)
+    t_copy = graph_timed([lambda: dst.copy_(src)] * 4, reps=3)
     del src, dst
+    small = {}
+    for traffic in (8388608, 16777216):
+        m = traffic // 2 // 4
+        bufs = [(torch.ones(m, device="cuda"), torch.empty(m, device="cuda")) for _ in range(32)]
+        t = graph_timed([lambda a=a, b=b: b.copy_(a) for a, b in bufs], reps=5)
+        small[f"{traffic / 1e6:.1f}MB"] = round(traffic / t / 1e9, 1)
+        del bufs
     S = 8192
     A = torch.randn(S, S, device="cuda").to(torch.bfloat16)
     W = torch.randn(S, S, device="cuda").mul_(0.02).to(torch.bfloat16)
+    Wt = W.t().contiguous()
     C = torch.empty(S, S, device="cuda")
-    t_gemm = timed(lambda: ops.gemm(L.DLM_EPI_STORE_F32, A, W, C=C), 10)
-    del A, W, C
+    Cb = torch.empty(S, S, device="cuda", dtype=torch.bfloat16)
+    t_ours = graph_timed([lambda: ops.gemm(L.DLM_EPI_STORE_F32, A, W, C=C)] * 4, reps=3)
+    t_blas = graph_timed([lambda: torch.mm(A, Wt, out=Cb)] * 4, reps=3)
+    del A, W, Wt, C, Cb
+    per_shape = {}
+    for name, (N, K) in STEP_GEMMS.items():
+        A = torch.randn(step_m, K, device="cuda").to(torch.bfloat16)
+        W = torch.randn(N, K, device="cuda").mul_(0.02).to(torch.bfloat16)
+        dual = name == "gemm_gate_up"
+        Wb = torch.randn(2 * N if dual else N, K, device="cuda").mul_(0.02).to(torch.bfloat16)
+        Wbt = Wb.t().contiguous()
+        Cb = torch.empty(step_m, Wb.shape[0], device="cuda", dtype=torch.bfloat16)
+        t_b = graph_timed([lambda: torch.mm(A, Wbt, out=Cb)] * 8)
+        if dual:
+            W2 = torch.randn(N, K, device="cuda").mul_(0.02).to(torch.bfloat16)
+            U = torch.empty(step_m, N, device="cuda", dtype=torch.bfloat16)
+            t_o = graph_timed([lambda: ops.gemm(L.DLM_EPI_SWIGLU, A, W, W2=W2, C=U)] * 8)
+        else:
+            Co = torch.empty(step_m, N, device="cuda")
+            t_o = graph_timed([lambda: ops.gemm(L.DLM_EPI_STORE_F32, A, W, C=Co)] * 8)
+        fl = 2.0 * step_m * Wb.shape[0] * K
+        per_shape[name] = dict(hipblaslt_us=round(t_b * 1e6, 2), ours_us=round(t_o * 1e6, 2),
+                               hipblaslt_tflops=round(fl / t_b / 1e12, 1),
+                               ours_tflops=round(fl / t_o / 1e12, 1))
+        del A, W, Wb, Wbt, Cb
     torch.cuda.empty_cache()
     return dict(hbm_copy_gbs=round(2 * 4 * n / t_copy / 1e9, 1),
-                gemm_bf16_tflops=round(2.0 * S ** 3 / t_gemm / 1e12, 1),
-                note="1 GiB device copy (read + write); this library's GEMM, 8192^3 bf16, "
-                     "default plan")
+                small_copy_gbs=small,
+                gemm_bf16_tflops_hipblaslt=round(2.0 * S ** 3 / t_blas / 1e12, 1),
+                gemm_bf16_tflops_ours=round(2.0 * S ** 3 / t_ours / 1e12, 1),
+                step_gemms_at_m=step_m, step_gemms=per_shape,
+                note="copies: read + write bytes; GEMMs graph-timed, 8192^3 bf16 "
+                     "(hipBLASLt via torch.mm, bf16 out; ours fp32 out)")
 
 
 def cpu_baseline(shape, run):
@@ -372,6 +447,8 @@ def main():
                     help="extra timed regions of the configured setting (spread only)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured copy / GEMM ceilings")
+    ap.add_argument("--no-whole-runs", action="store_true",
+                    help="skip the whole 128-step runs of the lock settings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 1 GiB device copies (counter calibration for profiles)")
     args = ap.parse_args()
@@ -406,6 +483,25 @@ def main():
         log(f"[{s}] {K} steps in {dt * 1e3:.1f} ms -> {K / dt:.1f} steps/s, "
             f"{toks / dt:.1f} tokens/s, mean M {sum(ms) / len(ms):.1f}")
         results[s] = dict(seconds=dt, tokens=toks, ms=ms)
+
+    # whole 128-step runs of the lock settings, whatever --steps is: the
+    # scheduled setting's locking shows only over a whole run
+    whole = {}
+    if not args.no_whole_runs:
+        for s in ("natural", "scheduled", "vanilla"):
+            run_steps(factory(s), run.steps)
+            fls = []
+            dt, toks, ms, _ = run_steps(factory(s), run.steps, flops_out=fls)
+            fl = sum(fls)
+            whole[s] = dict(steps=run.steps, seconds=round(dt, 4),
+                            steps_per_s=round(run.steps / dt, 3), tokens_per_s=round(toks / dt, 2),
+                            mean_active_rows=round(sum(ms) / len(ms), 1), tflop=round(fl / 1e12, 3))
+            log(f"[whole run/{s}] {run.steps} steps in {dt:.3f} s -> {run.steps / dt:.1f} steps/s, "
+                f"mean M {sum(ms) / len(ms):.1f}")
+        v = whole["vanilla"]
+        for s in ("natural", "scheduled"):
+            whole[s]["speedup_vs_vanilla"] = round(v["seconds"] / whole[s]["seconds"], 3)
+            whole[s]["flop_saving_vs_vanilla"] = round(1.0 - whole[s]["tflop"] / v["tflop"], 4)
 
     # the configured setting's timed region again, for its run-to-run spread
     spread = [K / nat_dt for nat_dt in (run_steps(factory("natural"), K)[0]
@@ -455,6 +551,11 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if whole:
+        out["whole_run"] = dict(whole, note="one whole run per setting (timed after one whole "
+                                             "warm-up run); FLOPs as the engine counts them per "
+                                             "step (projections, FFN, attention, LM head on the "
+                                             "active rows)")
     for s in settings[1:]:
         r = results[s]
         out[f"{s}_lock"] = dict(steps_per_s=round(K / r["seconds"], 3),
@@ -467,12 +568,20 @@ def main():
         log("measured ceilings ...")
         out["ceilings"] = measured_ceilings()
         ach = out["roofline"]["achieved"]
-        ceil = out["ceilings"]["gemm_bf16_tflops" if out["roofline"]["bound"] == "mfma"
+        ceil = out["ceilings"]["gemm_bf16_tflops_hipblaslt" if out["roofline"]["bound"] == "mfma"
                                else "hbm_copy_gbs"]
         out["roofline"]["frac_of_measured_ceiling"] = round(ach / ceil, 4) if ceil else None
+        out["roofline"]["measured_ceiling"] = ("hipBLASLt 8192^3 bf16" if
+                                               out["roofline"]["bound"] == "mfma" else
+                                               "1 GiB device copy")
     if not args.no_layer_sweep:
         log("single-layer roofline sweep ...")
         out["layer_isolation"] = layer_isolation()
+        floor = out.get("ceilings", {}).get("small_copy_gbs", {}).get("16.8MB")
+        if floor:
+            for pt in out["layer_isolation"]["points"]:
+                pt["attention_frac_of_small_copy"] = round(pt["attention_gbs"] / floor, 4)
+            out["layer_isolation"]["small_copy_gbs"] = floor
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(shape, run)
