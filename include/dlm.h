@@ -232,6 +232,15 @@ int dlm_get(dlm_handle* h, int32_t what, const void** dev_ptr, int64_t* n);
  * rows, attention of M_t queries over N keys, plus the LM head). */
 int dlm_last_step_info(const dlm_handle* h, int32_t* step, int32_t* m_tot, double* flops);
 
+/* Debug aid: fills every state array that a step writes before it reads
+ * (the per-layer K/V cache, both logit buffers and log-normalisers, the
+ * per-row statistics, the activations and the workspace) with a quiet NaN
+ * pattern, so that a read of a value no step wrote shows up as a NaN in a
+ * logit or statistic.  Tokens, lock bits, counters and flags keep what
+ * dlm_step_init wrote.  Only before the first dlm_step (DLM_E_STATE
+ * otherwise); enqueued on the handle's stream. */
+int dlm_debug_poison(dlm_handle* h);
+
 /* Frees the handle (not state_mem).  Waits for the stream. */
 int dlm_destroy(dlm_handle* h);
 

@@ -38,7 +38,7 @@ EXPORTS = [
     "dlm_op_vocab_stats", "dlm_op_lm_head_stats_ws_bytes", "dlm_op_lm_head_stats",
     "dlm_op_commit_lock", "dlm_op_slowfast_commit", "dlm_op_gemm_noalloc_max_bytes",
     "dlm_op_gemm_noalloc", "dlm_op_attention_num_layouts", "dlm_op_attention_layout_ws_bytes",
-    "dlm_op_attention_layout",
+    "dlm_op_attention_layout", "dlm_debug_poison",
 ]
 
 i32 = ctypes.c_int32
@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
         L.dlm_get.argtypes = [vp, i32, P(vp), P(ctypes.c_int64)]
         L.dlm_last_step_info.argtypes = [vp, P(i32), P(i32), P(ctypes.c_double)]
         L.dlm_destroy.argtypes = [vp]
+        L.dlm_debug_poison.argtypes = [vp]
         L.dlm_error_string.restype = ctypes.c_char_p
         L.dlm_error_string.argtypes = [ctypes.c_int]
         L.dlm_set_timing.argtypes = [vp, i32]

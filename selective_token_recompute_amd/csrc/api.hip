@@ -644,6 +644,31 @@ int dlm_get(dlm_handle* h, int32_t what, const void** dev_ptr, int64_t* n) {
   return DLM_OK;
 }
 
+int dlm_debug_poison(dlm_handle* h) {
+  if (!h) return DLM_E_INVALID;
+  if (h->t != 0 || h->stepped) return DLM_E_STATE;
+  const Layout& y = h->lay;
+  const dlm_model_desc& m = h->m;
+  const size_t B = h->r.batch, N = h->r.seq_len, BN = B * N;
+  const size_t es = m.dtype == DLM_BF16 ? 2 : 4;
+  const size_t d = m.d_model, qo = (size_t)m.n_heads * m.head_dim;
+  const size_t qkv = (size_t)(m.n_heads + 2 * m.n_kv_heads) * m.head_dim;
+  const size_t kvn = (size_t)m.n_layers * B * m.n_kv_heads * N * m.head_dim;
+  // 0x7FC07FC0 is a quiet NaN as one float and as each of two bfloat16s
+  const uint32_t nan2 = 0x7FC07FC0u;
+  const struct { size_t off, bytes; } regions[] = {
+      {y.z[0], BN * m.vocab * 4}, {y.z[1], BN * m.vocab * 4}, {y.lse[0], BN * 4},
+      {y.lse[1], BN * 4},         {y.kc, kvn * es},           {y.vc, kvn * es},
+      {y.h, BN * d * 4},          {y.a, BN * d * es},         {y.qkv, BN * qkv * 4},
+      {y.q, BN * qo * es},        {y.o, BN * qo * es},        {y.u, BN * m.d_ff * es},
+      {y.ws, y.ws_bytes},         {y.argmax, BN * 4},         {y.conf, BN * 4},
+      {y.kl, BN * 4},             {y.has_kl, BN * 4},         {y.lse_row, BN * 4},
+      {y.row_real, BN * 4}};
+  for (const auto& r : regions)
+    TRY(launch_fill_u32(h->base + r.off, r.bytes, nan2, h->stream));
+  return DLM_OK;
+}
+
 int dlm_last_step_info(const dlm_handle* h, int32_t* step, int32_t* m_tot, double* flops) {
   if (!h) return DLM_E_INVALID;
   if (step) *step = h->last_t;

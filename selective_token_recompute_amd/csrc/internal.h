@@ -170,6 +170,8 @@ hipError_t launch_apply_override(int B, int N, int n_commit, const int32_t* cseq
                                  const int32_t* cpos, const int32_t* ctok, const uint64_t* bits_or,
                                  const int32_t* counters, int32_t* tokens, uint64_t* bits,
                                  int32_t* cnt, hipStream_t s);
+// Fills bytes / 4 words at p with the pattern v.
+hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t v, hipStream_t s);
 hipError_t launch_init_state(int B, int N, int P, int mask_id, const int32_t* prompts,
                              int32_t* tokens, uint64_t* bits, int32_t* counters,
                              int32_t* has_prev, int32_t* ctl, uint64_t* frozen,

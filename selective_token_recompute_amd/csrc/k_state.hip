@@ -53,6 +53,22 @@ hipError_t launch_init_state(int B, int N, int P, int mask_id, const int32_t* pr
 }
 
 // ---------------------------------------------------------------------------
+// Fill of a buffer with a 32-bit pattern (a kernel, not a memset, so that it
+// may sit in a captured graph).
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t v, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  const int grid = (int)std::min<size_t>((n + 255) / 256, 8192);
+  fill_u32_kernel<<<grid, 256, 0, s>>>((uint32_t*)p, n, v);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Compaction: one workgroup of 1024 threads scans the B*N positions in
 // (seq, pos) order, 1024 at a time.  Each wave ballots its 64 "active"

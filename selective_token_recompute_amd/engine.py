@@ -151,8 +151,14 @@ class Engine:
     """One decoding run on the GPU through the C ABI."""
 
     def __init__(self, shape, dev_weights: Dict, run, lock: Dict, prompts: torch.Tensor,
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None, metrics_path: Optional[str] = None):
+        """metrics_path: if given, every lock_update appends one JSON line
+        {t, m_tot, m_b, commits, new_locks, locked, flops} to that file (the
+        step's active rows per sequence, positions unmasked and locked by the
+        update, locked positions in all, the step's algorithmic FLOPs); this
+        reads small arrays back to the host each step."""
         self.shape, self.run, self.lock = shape, run, lock
+        self.metrics_path = metrics_path
         self.device = prompts.device
         self.stream = stream
         self.dw = dev_weights
@@ -184,10 +190,18 @@ class Engine:
         self.m = dlm_step(self.h)
         return self.m
 
+    def debug_poison(self) -> None:
+        """dlm_debug_poison: NaN in every array a step writes before it reads
+        (only before the first step)."""
+        L.check(L.lib().dlm_debug_poison(self.h), "dlm_debug_poison")
+
     def lock_update(self, commits=None, lock_bits=None, counters=None) -> None:
         """commits: (seq, pos, tok) int sequences replacing the top-k choice;
         lock_bits: uint64 numpy [B][W] ORed in instead of the lock test;
         counters: int32 numpy [B][N] (with lock_bits)."""
+        if self.metrics_path:
+            tok0 = self.tokens().clone()
+            bits0 = self.lock_bits().clone()
         if commits is None and lock_bits is None:
             dlm_lock_update(self.h, None)
         else:
@@ -210,7 +224,26 @@ class Engine:
                 if counters is not None:
                     ov.counters = arr(counters, np.int32)
             dlm_lock_update(self.h, ov)
+        if self.metrics_path:
+            self._write_metrics(tok0, bits0)
         self.t += 1
+
+    def _write_metrics(self, tok0: torch.Tensor, bits0: torch.Tensor) -> None:
+        import json
+
+        import numpy as np
+
+        def nbits(b: torch.Tensor) -> int:
+            return int(np.unpackbits(b.cpu().numpy().view(np.uint8)).sum())
+
+        step, m, flops = self.last_step_info()
+        rs = self.rows()[0][:m].cpu().numpy() if m else np.zeros(0, np.int32)
+        bits1 = self.lock_bits()
+        rec = dict(t=step, m_tot=m, m_b=np.bincount(rs, minlength=self.run.batch).tolist(),
+                   commits=int((self.tokens() != tok0).sum().item()),
+                   new_locks=nbits(bits1 & ~bits0), locked=nbits(bits1), flops=flops)
+        with open(self.metrics_path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
 
     def _view(self, what: int, dtype: torch.dtype, shape=None) -> torch.Tensor:
         p, n = dlm_get(self.h, what)

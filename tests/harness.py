@@ -163,11 +163,15 @@ def explain_difference(shape, run, lock, t, x_before, x_g, x_o, lk_g, lk_o, cnt_
 
 
 def run_lockstep(shape, W: Dict, run, lock: Dict, prompts: np.ndarray, steps: Optional[int] = None,
-                 dev_weights: Optional[Dict] = None, check=True) -> List[StepReport]:
-    """Runs `steps` steps on engine and oracle in lockstep; asserts parity."""
+                 dev_weights: Optional[Dict] = None, check=True,
+                 poison=False) -> List[StepReport]:
+    """Runs `steps` steps on engine and oracle in lockstep; asserts parity.
+    poison: fill the engine's write-before-read state with NaN first."""
     dev = torch.device("cuda")
     dw = dev_weights if dev_weights is not None else E.upload_weights(W, shape, dev)
     eng = E.Engine(shape, dw, run, lock, torch.from_numpy(prompts).to(dev))
+    if poison:
+        eng.debug_poison()
     orc = oracle.Oracle(shape, W, run, lock, prompts)
     B, N, V = run.batch, run.seq_len, shape.vocab
     reports = []

@@ -90,6 +90,100 @@ def test_tiny_bf16_generic_path():
     _report("tiny-bf16/scheduled", run_lockstep(shape, W, run, synth.LOCK_SETTINGS["scheduled"], pr))
 
 
+@pytest.mark.parametrize("case", ["tiny-fp32", "mid-bf16", "mid-gqa-bf16"])
+def test_poisoned_state_is_never_read(tiny, case):
+    """Every array a step writes before it reads starts as NaN
+    (dlm_debug_poison); the lockstep against the oracle still holds every
+    logit and statistic finite and within tolerance, so no step reads a
+    value it did not write (K/V of positions not yet computed, previous
+    logits of rows without a previous posterior, workspace, activations)."""
+    if case == "tiny-fp32":
+        shape, run, W, pr = tiny
+        steps = run.steps
+    else:
+        shape = MID if case == "mid-bf16" else MID_GQA
+        run, W, pr = MID_RUN, synth.gen_weights(shape), synth.gen_prompts(shape, MID_RUN)
+        steps = 10
+    reps = run_lockstep(shape, W, run, synth.LOCK_SETTINGS["scheduled"], pr, steps=steps,
+                        poison=True)
+    assert len(reps) == steps and all(np.isfinite(r.max_dz) for r in reps)
+
+
+def test_per_step_metrics_record(tiny, tmp_path):
+    """The engine's per-step JSON-lines record against the oracle's own
+    trajectory: active rows, unmasked count, new locks, FLOPs."""
+    import json
+    shape, run, W, pr = tiny
+    lock = synth.LOCK_SETTINGS["scheduled"]
+    dev = torch.device("cuda")
+    path = str(tmp_path / "metrics.jsonl")
+    eng = E.Engine(shape, E.upload_weights(W, shape, dev), run, lock,
+                   torch.from_numpy(pr).to(dev), metrics_path=path)
+    orc = oracle.Oracle(shape, W, run, lock, pr)
+    want = []
+    for t in range(run.steps):
+        eng.step()
+        orc.step()
+        before = orc.locked().copy()
+        orc.lock_update()
+        eng.lock_update()
+        want.append(dict(m=orc.m, commits=len(orc.commits()[0]),
+                         new=int((orc.locked() & ~before).sum()), locked=int(orc.locked().sum())))
+    eng.close()
+    got = [json.loads(line) for line in open(path)]
+    assert [g["t"] for g in got] == list(range(run.steps))
+    for g, w in zip(got, want):
+        assert g["m_tot"] == w["m"] == sum(g["m_b"])
+        assert g["commits"] == w["commits"]
+        assert g["new_locks"] == w["new"] and g["locked"] == w["locked"]
+        assert g["flops"] == pytest.approx(oracle.closed_form_flops(shape, [w["m"]], run.seq_len))
+
+
+def test_same_run_twice_is_bitwise_identical(llada_weights):
+    """Determinism: two engines on the same LLaDA-8B-shaped run (full width,
+    32 layers, scheduled locking, the first 6 steps: M = 512, 384, ...) give
+    bitwise identical logits, statistics, tokens, lock bits and counters at
+    every step (every reduction runs in a fixed order)."""
+    shape, run = synth.CONFIGS["llada8b"]
+    lock = synth.LOCK_SETTINGS["scheduled"]
+    pr = torch.from_numpy(synth.gen_prompts(shape, run)).cuda()
+    e1 = E.Engine(shape, llada_weights, run, lock, pr)
+    e2 = E.Engine(shape, llada_weights, run, lock, pr)
+    for t in range(6):
+        m1, m2 = e1.step(), e2.step()
+        assert m1 == m2
+        rs, rp = (a[:m1].long() for a in e1.rows()[:2])
+        assert torch.equal(e1.logits()[rs, rp].view(torch.int32),
+                           e2.logits()[rs, rp].view(torch.int32)), f"step {t}: logits"
+        s1, s2 = e1.stats(), e2.stats()
+        for k in s1:
+            assert torch.equal(s1[k][:m1].view(torch.int32), s2[k][:m1].view(torch.int32)), k
+        e1.lock_update()
+        e2.lock_update()
+        assert torch.equal(e1.tokens(), e2.tokens()) and torch.equal(e1.lock_bits(), e2.lock_bits())
+        assert torch.equal(e1.counters(), e2.counters())
+        kc1, vc1 = e1.kv_cache()
+        kc2, vc2 = e2.kv_cache()
+        assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16))
+        assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16))
+    e1.close()
+    e2.close()
+
+
+def test_poison_only_before_the_first_step(tiny):
+    shape, run, W, pr = tiny
+    dev = torch.device("cuda")
+    eng = E.Engine(shape, E.upload_weights(W, shape, dev), run, synth.LOCK_SETTINGS["natural"],
+                   torch.from_numpy(pr).to(dev))
+    eng.debug_poison()
+    eng.step()
+    from selective_token_recompute_amd._lib import DLM_E_STATE, DlmError
+    with pytest.raises(DlmError) as ei:
+        eng.debug_poison()
+    assert ei.value.status == DLM_E_STATE
+    eng.close()
+
+
 def test_empty_active_set_and_forced_locks(tiny):
     """Every row force-locked: the next step has M = 0 and is a no-op."""
     shape, run, W, pr = tiny
