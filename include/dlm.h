@@ -241,6 +241,33 @@ int dlm_last_step_info(const dlm_handle* h, int32_t* step, int32_t* m_tot, doubl
  * otherwise); enqueued on the handle's stream. */
 int dlm_debug_poison(dlm_handle* h);
 
+/* Checkpoint of a run at a step boundary, for resuming it or replaying it
+ * from a chosen step.  The pages define no checkpoint; the image holds the
+ * state a later step reads (SureLock page, §2 Methodology): the tokens, the
+ * lock bitmask and consecutive-pass counters, the previous-posterior flags,
+ * log-normalisers and logits that the next step's KL reads, the per-layer
+ * K/V cache that locked positions keep attending to, the SlowFast cycle
+ * state and frozen set, the last step's per-row arrays and the device's
+ * latched numeric flag, plus the host counters (step index, last active count
+ * and FLOPs) and a copy of the model and run descriptors.  The layout is
+ * private to this library and version.
+ *
+ * dlm_checkpoint_bytes: size of the image for this handle (0 for null).
+ * dlm_checkpoint_save: writes the image to dst, host or device memory of at
+ *   least that size (owned by the caller); returns once the copy is complete.
+ * dlm_checkpoint_load: restores an image into a handle made with the same
+ *   model and run descriptors (byte for byte), at any step; the weights are
+ *   the handle's own.  After it the handle continues exactly as the saved
+ *   one would have (same kernels, same order: the steps that follow are
+ *   bitwise those of the uninterrupted run).
+ * Errors: DLM_E_INVALID (null pointer; on load a bad header or descriptors
+ * that differ), DLM_E_STATE (a step is pending its dlm_lock_update),
+ * DLM_E_SIZE (buffer smaller than dlm_checkpoint_bytes), DLM_E_HIP (a copy
+ * failed; after a failed load the state is undefined). */
+size_t dlm_checkpoint_bytes(const dlm_handle* h);
+int dlm_checkpoint_save(dlm_handle* h, void* dst, size_t dst_bytes);
+int dlm_checkpoint_load(dlm_handle* h, const void* src, size_t src_bytes);
+
 /* Frees the handle (not state_mem).  Waits for the stream. */
 int dlm_destroy(dlm_handle* h);
 

@@ -39,6 +39,7 @@ EXPORTS = [
     "dlm_op_commit_lock", "dlm_op_slowfast_commit", "dlm_op_gemm_noalloc_max_bytes",
     "dlm_op_gemm_noalloc", "dlm_op_attention_num_layouts", "dlm_op_attention_layout_ws_bytes",
     "dlm_op_attention_layout", "dlm_debug_poison",
+    "dlm_checkpoint_bytes", "dlm_checkpoint_save", "dlm_checkpoint_load",
 ]
 
 i32 = ctypes.c_int32
@@ -102,6 +103,10 @@ def lib() -> ctypes.CDLL:
         L.dlm_last_step_info.argtypes = [vp, P(i32), P(i32), P(ctypes.c_double)]
         L.dlm_destroy.argtypes = [vp]
         L.dlm_debug_poison.argtypes = [vp]
+        L.dlm_checkpoint_bytes.restype = sz
+        L.dlm_checkpoint_bytes.argtypes = [vp]
+        L.dlm_checkpoint_save.argtypes = [vp, vp, sz]
+        L.dlm_checkpoint_load.argtypes = [vp, vp, sz]
         L.dlm_error_string.restype = ctypes.c_char_p
         L.dlm_error_string.argtypes = [ctypes.c_int]
         L.dlm_set_timing.argtypes = [vp, i32]

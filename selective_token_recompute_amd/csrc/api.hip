@@ -669,6 +669,120 @@ int dlm_debug_poison(dlm_handle* h) {
   return DLM_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// Checkpoint image: a 256-byte header, then three byte ranges of the state
+// copied as they lie: the per-position and per-row arrays (tokens through
+// the two log-normaliser buffers, contiguous in the layout), the logits
+// buffer the next step reads as the previous posterior, and the K and V
+// caches (contiguous).
+constexpr char kCkptMagic[8] = {'D', 'L', 'M', 'C', 'K', 'P', 'T', '1'};
+constexpr uint32_t kCkptVersion = 1;
+constexpr size_t kCkptHeaderBytes = 256;
+static_assert(sizeof(dlm_model_desc) == 11 * 4, "model descriptor without padding");
+static_assert(sizeof(dlm_run_desc) == 18 * 4, "run descriptor without padding");
+
+struct CkptHeader {
+  char magic[8];
+  uint32_t version, header_bytes;
+  dlm_model_desc m;
+  dlm_run_desc r;
+  int32_t t, last_t, M, reserved;
+  double flops;
+  uint64_t small_bytes, z_bytes, kv_bytes, total;
+};
+static_assert(sizeof(CkptHeader) <= kCkptHeaderBytes, "checkpoint header");
+
+struct CkptParts {
+  size_t small_off, small_bytes, z_bytes, kv_off, kv_bytes, total;
+};
+
+CkptParts ckpt_parts(const dlm_handle* h) {
+  const Layout& y = h->lay;
+  CkptParts c;
+  c.small_off = y.tokens;
+  c.small_bytes = y.z[0] - y.tokens;
+  c.z_bytes = (size_t)h->r.batch * h->r.seq_len * h->m.vocab * 4;
+  c.kv_off = y.kc;
+  c.kv_bytes = y.rope - y.kc;
+  c.total = kCkptHeaderBytes + c.small_bytes + c.z_bytes + c.kv_bytes;
+  return c;
+}
+
+// logits buffer that the handle's next step reads as the previous posterior
+size_t ckpt_prev_z(const dlm_handle* h) { return h->lay.z[(h->t & 1) ^ 1]; }
+}  // namespace
+
+extern "C" {
+
+size_t dlm_checkpoint_bytes(const dlm_handle* h) { return h ? ckpt_parts(h).total : 0; }
+
+int dlm_checkpoint_save(dlm_handle* h, void* dst, size_t dst_bytes) {
+  if (!h || !dst) return DLM_E_INVALID;
+  if (h->stepped) return DLM_E_STATE;
+  const CkptParts c = ckpt_parts(h);
+  if (dst_bytes < c.total) return DLM_E_SIZE;
+  unsigned char hd_bytes[kCkptHeaderBytes] = {};
+  CkptHeader hd{};
+  std::memcpy(hd.magic, kCkptMagic, sizeof(kCkptMagic));
+  hd.version = kCkptVersion;
+  hd.header_bytes = (uint32_t)kCkptHeaderBytes;
+  hd.m = h->m;
+  hd.r = h->r;
+  hd.t = h->t;
+  hd.last_t = h->last_t;
+  hd.M = h->M;
+  hd.flops = h->flops;
+  hd.small_bytes = c.small_bytes;
+  hd.z_bytes = c.z_bytes;
+  hd.kv_bytes = c.kv_bytes;
+  hd.total = c.total;
+  std::memcpy(hd_bytes, &hd, sizeof(hd));
+  unsigned char* d = static_cast<unsigned char*>(dst);
+  TRY(hipMemcpyAsync(d, hd_bytes, kCkptHeaderBytes, hipMemcpyDefault, h->stream));
+  d += kCkptHeaderBytes;
+  TRY(hipMemcpyAsync(d, h->base + c.small_off, c.small_bytes, hipMemcpyDefault, h->stream));
+  d += c.small_bytes;
+  TRY(hipMemcpyAsync(d, h->base + ckpt_prev_z(h), c.z_bytes, hipMemcpyDefault, h->stream));
+  d += c.z_bytes;
+  TRY(hipMemcpyAsync(d, h->base + c.kv_off, c.kv_bytes, hipMemcpyDefault, h->stream));
+  TRY(hipStreamSynchronize(h->stream));  // hd_bytes lives on this stack frame
+  return DLM_OK;
+}
+
+int dlm_checkpoint_load(dlm_handle* h, const void* src, size_t src_bytes) {
+  if (!h || !src) return DLM_E_INVALID;
+  if (h->stepped) return DLM_E_STATE;
+  const CkptParts c = ckpt_parts(h);
+  if (src_bytes < c.total) return DLM_E_SIZE;
+  CkptHeader hd{};
+  TRY(hipMemcpyAsync(&hd, src, sizeof(hd), hipMemcpyDefault, h->stream));
+  TRY(hipStreamSynchronize(h->stream));
+  const int64_t BN = (int64_t)h->r.batch * h->r.seq_len;
+  const bool ok =
+      std::memcmp(hd.magic, kCkptMagic, sizeof(kCkptMagic)) == 0 &&
+      hd.version == kCkptVersion && hd.header_bytes == kCkptHeaderBytes &&
+      std::memcmp(&hd.m, &h->m, sizeof(dlm_model_desc)) == 0 &&
+      std::memcmp(&hd.r, &h->r, sizeof(dlm_run_desc)) == 0 && hd.small_bytes == c.small_bytes &&
+      hd.z_bytes == c.z_bytes && hd.kv_bytes == c.kv_bytes && hd.total == c.total &&
+      hd.t >= 0 && hd.t <= h->r.steps && hd.last_t == hd.t - 1 && hd.M >= 0 && hd.M <= BN;
+  if (!ok) return DLM_E_INVALID;
+  h->t = hd.t;  // fixes which logits buffer the next step reads as the previous one
+  const unsigned char* s = static_cast<const unsigned char*>(src) + kCkptHeaderBytes;
+  TRY(hipMemcpyAsync(h->base + c.small_off, s, c.small_bytes, hipMemcpyDefault, h->stream));
+  s += c.small_bytes;
+  TRY(hipMemcpyAsync(h->base + ckpt_prev_z(h), s, c.z_bytes, hipMemcpyDefault, h->stream));
+  s += c.z_bytes;
+  TRY(hipMemcpyAsync(h->base + c.kv_off, s, c.kv_bytes, hipMemcpyDefault, h->stream));
+  TRY(hipStreamSynchronize(h->stream));
+  h->last_t = hd.last_t;
+  h->M = hd.M;
+  h->flops = hd.flops;
+  h->stepped = false;
+  return DLM_OK;
+}
+
 int dlm_last_step_info(const dlm_handle* h, int32_t* step, int32_t* m_tot, double* flops) {
   if (!h) return DLM_E_INVALID;
   if (step) *step = h->last_t;

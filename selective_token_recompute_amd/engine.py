@@ -8,6 +8,7 @@ from __future__ import annotations
 import ctypes
 from typing import Dict, List, Optional
 
+import numpy as np
 import torch
 
 from . import _lib as L
@@ -80,6 +81,31 @@ def dlm_get(h, what: int):
     n = ctypes.c_int64()
     L.check(L.lib().dlm_get(h, what, ctypes.byref(p), ctypes.byref(n)), "dlm_get")
     return int(p.value or 0), int(n.value)
+
+
+def dlm_checkpoint_bytes(h) -> int:
+    return int(L.lib().dlm_checkpoint_bytes(h))
+
+
+def dlm_checkpoint_save(h, dst_ptr: int, dst_bytes: int) -> None:
+    L.check(L.lib().dlm_checkpoint_save(h, ctypes.c_void_p(dst_ptr), dst_bytes),
+            "dlm_checkpoint_save")
+
+
+def dlm_checkpoint_load(h, src_ptr: int, src_bytes: int) -> None:
+    L.check(L.lib().dlm_checkpoint_load(h, ctypes.c_void_p(src_ptr), src_bytes),
+            "dlm_checkpoint_load")
+
+
+def _buffer(buf):
+    """(address, bytes) of a C-contiguous numpy array or torch tensor."""
+    if isinstance(buf, np.ndarray):
+        if not buf.flags["C_CONTIGUOUS"]:
+            raise ValueError("checkpoint buffer must be contiguous")
+        return buf.ctypes.data, buf.nbytes
+    if not buf.is_contiguous():
+        raise ValueError("checkpoint buffer must be contiguous")
+    return buf.data_ptr(), buf.numel() * buf.element_size()
 
 
 def dlm_destroy(h) -> None:
@@ -194,6 +220,24 @@ class Engine:
         """dlm_debug_poison: NaN in every array a step writes before it reads
         (only before the first step)."""
         L.check(L.lib().dlm_debug_poison(self.h), "dlm_debug_poison")
+
+    def checkpoint_bytes(self) -> int:
+        return dlm_checkpoint_bytes(self.h)
+
+    def save_checkpoint(self, out=None):
+        """dlm_checkpoint_save at a step boundary into `out` (a contiguous
+        numpy array or torch tensor, host or device, of at least
+        checkpoint_bytes()); without `out` a new host uint8 array is
+        returned."""
+        if out is None:
+            out = np.empty(self.checkpoint_bytes(), dtype=np.uint8)
+        dlm_checkpoint_save(self.h, *_buffer(out))
+        return out
+
+    def load_checkpoint(self, buf) -> None:
+        """dlm_checkpoint_load from an image written by save_checkpoint of a
+        handle with the same model and run descriptors."""
+        dlm_checkpoint_load(self.h, *_buffer(buf))
 
     def lock_update(self, commits=None, lock_bits=None, counters=None) -> None:
         """commits: (seq, pos, tok) int sequences replacing the top-k choice;

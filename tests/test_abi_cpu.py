@@ -126,6 +126,10 @@ def test_null_handle_calls():
     assert lib.dlm_get(None, 0, ctypes.byref(p), ctypes.byref(n)) == L.DLM_E_INVALID
     assert lib.dlm_destroy(None) == L.DLM_E_INVALID
     assert lib.dlm_set_timing(None, 1) == L.DLM_E_INVALID
+    assert lib.dlm_checkpoint_bytes(None) == 0
+    buf = ctypes.create_string_buffer(64)
+    assert lib.dlm_checkpoint_save(None, buf, 64) == L.DLM_E_INVALID
+    assert lib.dlm_checkpoint_load(None, buf, 64) == L.DLM_E_INVALID
 
 
 def test_op_argument_validation():
