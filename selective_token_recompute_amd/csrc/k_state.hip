@@ -155,10 +155,123 @@ hipError_t launch_compact(const uint64_t* bits, const uint64_t* frozen, int B, i
 
 // ---------------------------------------------------------------------------
 // Commit + lock, one workgroup per sequence.
-// Candidates (masked rows of the current block) are gathered in LDS; each
-// candidate's rank is the number of candidates strictly ahead of it in the
-// order (conf descending, position ascending); ranks below k commit.
+// Candidates (masked rows of the current block) are gathered in LDS in row
+// order; each candidate's rank is the number of candidates strictly ahead of
+// it in the order (conf descending, position ascending); ranks below k
+// commit.
 constexpr int kLockThreads = 1024;
+constexpr int kLockWaves = kLockThreads / 64;
+
+// Key whose unsigned order is the commit order: confidence descending, then
+// position ascending.  The confidence's bits are mapped to an unsigned
+// integer of the same order (-0 taken as +0, so the two tie as floats do);
+// the low half is INT_MAX - pos.  Every key is above 0, the padding key.
+// (Confidences are maxima of a softmax: never NaN on a step that decides.)
+__device__ __forceinline__ uint64_t rank_key(float conf, int pos) {
+  uint32_t u = __float_as_uint(conf + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0x7fffffff - pos);
+}
+__device__ __forceinline__ int key_pos(uint64_t key) {
+  return 0x7fffffff - (int)(uint32_t)key;
+}
+
+// Gathers the rows r0 .. r1-1 for which take(pos) holds into (cconf, cpos,
+// crow), in row order: a wave ballot gives each lane its slot among its
+// wave's candidates and per-wave counts give the waves' offsets (a shared
+// counter bumped by every candidate would serialise them).  Returns the
+// number gathered, at most cap (the positions a candidate can hold, distinct
+// for distinct rows), with each candidate's rank key, and pads the arrays to
+// the next multiple of 16 (their length; padding keys are 0, behind every
+// candidate); every thread of the workgroup calls it.
+template <typename Take>
+__device__ int gather_candidates(const LockArgs& a, int r0, int r1, Take take, int cap,
+                                 uint64_t* ckey, float* cconf, int* cpos, int* crow) {
+  __shared__ int wcnt[kLockWaves];
+  __shared__ int s_base;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  for (int c0 = r0; c0 < r1; c0 += kLockThreads) {
+    const int r = c0 + tid;
+    int pos = 0;
+    float cf = 0.f;
+    bool t = false;
+    if (r < r1) {
+      pos = a.row_pos[r];
+      cf = a.conf[r];
+      t = take(pos);
+    }
+    const uint64_t bal = __ballot(t);
+    if (lane == 0) wcnt[wv] = __popcll(bal);
+    __syncthreads();
+    int off = s_base;
+    for (int w = 0; w < wv; ++w) off += wcnt[w];
+    const int slot = off + __popcll(bal & ((1ull << lane) - 1ull));
+    if (t && slot < cap) {
+      ckey[slot] = rank_key(cf, pos);
+      cconf[slot] = cf;
+      cpos[slot] = pos;
+      crow[slot] = r;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int n = s_base;
+      for (int w = 0; w < kLockWaves; ++w) n += wcnt[w];
+      s_base = n;
+    }
+    __syncthreads();
+  }
+  const int C = min(s_base, cap);
+  // pad to a multiple of 16 with entries that rank behind every candidate
+  if (tid < ((C + 15) & ~15) - C) {
+    ckey[C + tid] = 0ull;
+    cconf[C + tid] = -INFINITY;
+    cpos[C + tid] = 0x7fffffff;
+  }
+  __syncthreads();
+  return C;
+}
+
+// bits[pos / 64] |= 1 << (pos % 64) for the lanes with `set`: one atomic OR
+// per distinct word per wave (lanes whose positions share a word OR their
+// bits together first).  Every lane of the wave calls it.
+__device__ void or_position_bits(uint64_t* bits, bool set, int pos) {
+  const int lane = threadIdx.x & 63;
+  bool pending = set;
+  for (uint64_t pend = __ballot(pending); pend; pend = __ballot(pending)) {
+    const int leader = __ffsll((unsigned long long)pend) - 1;
+    const int w0 = __shfl(pos >> 6, leader);
+    const bool mine = pending && (pos >> 6) == w0;
+    unsigned long long v = mine ? (1ull << (pos & 63)) : 0ull;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o);
+    if (lane == leader) atomicOr((unsigned long long*)&bits[w0], v);
+    pending = pending && !mine;
+  }
+}
+
+// Rank of candidate c among the candidates whose position p has ok(p): the
+// number whose key is above c's, counted only up to `cap` (a candidate with
+// k candidates ahead of it is out of any top k).  16 keys per pass, read as
+// 16-byte LDS broadcasts; branch-free (the keys are the same for every lane,
+// and tests on them would otherwise compile to scalar branches).
+template <typename Ok>
+__device__ int rank_upto(int c, int C, const uint64_t* ckey, int cap, Ok ok) {
+  const uint64_t kc = ckey[c];
+  const int Cp = (C + 15) & ~15;
+  int rank = 0;
+  for (int j0 = 0; j0 < Cp && rank < cap; j0 += 16) {
+    ulonglong2 k2[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) k2[q] = *reinterpret_cast<const ulonglong2*>(ckey + j0 + 2 * q);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      rank += (int)((k2[q].x > kc) & (bool)ok(key_pos(k2[q].x))) +
+              (int)((k2[q].y > kc) & (bool)ok(key_pos(k2[q].y)));
+  }
+  return rank;
+}
 
 // SlowFast commit for sequence b ([SF] §2 two-stage pipeline), the rule of
 // the CPU reference in the same words: candidates are this step's rows still
@@ -175,8 +288,9 @@ constexpr int kLockThreads = 1024;
 // unfreeze, clear those positions' previous-posterior flag, reset the state.
 // State per sequence (kSfStateInts ints): phase, lo, hi, slow_n, hist_n,
 // hist[8].
-__device__ void slowfast_commit(const LockArgs& a, int b, int C, const float* cconf,
-                                const int* cpos, const int* crow, int s_front, int e_max) {
+__device__ void slowfast_commit(const LockArgs& a, int b, int C, const uint64_t* ckey,
+                                const float* cconf, const int* cpos, const int* crow,
+                                int s_front, int e_max) {
   __shared__ int sh_fast, sh_lo, sh_hi, sh_nhigh, sh_left;
   const int tid = threadIdx.x, N = a.N, W = (N + 63) >> 6;
   int32_t* st = a.sf_state + (size_t)b * kSfStateInts;
@@ -225,9 +339,9 @@ __device__ void slowfast_commit(const LockArgs& a, int b, int C, const float* cc
   __syncthreads();
   const int fast = sh_fast, lo = sh_lo, hi = sh_hi;
   // the candidate set of this step's commit rule
-  auto eligible = [&](int c) {
-    return fast ? (cpos[c] >= lo && cpos[c] < hi) : (cpos[c] < s_front + a.sf_window);
-  };
+  const int e_lo = fast ? lo : 0, e_hi = fast ? hi : s_front + a.sf_window;
+  auto eligible_pos = [&](int p) { return (p >= e_lo) & (p < e_hi); };
+  auto eligible = [&](int c) { return eligible_pos(cpos[c]); };
   if (fast) {
     int nh = 0;
     for (int c = tid; c < C; c += kLockThreads)
@@ -242,15 +356,7 @@ __device__ void slowfast_commit(const LockArgs& a, int b, int C, const float* cc
     if (by_threshold) {
       take = cconf[c] > a.sf_tau_high;
     } else {
-      const float cf = cconf[c];
-      const int cp = cpos[c];
-      int rank = 0;
-      for (int j = 0; j < C; ++j) {
-        if (!eligible(j)) continue;
-        const float f = cconf[j];
-        rank += (f > cf) || (f == cf && cpos[j] < cp);
-      }
-      take = rank < a.sf_k;
+      take = rank_upto(c, C, ckey, a.sf_k, eligible_pos) < a.sf_k;
     }
     if (take) tok[cpos[c]] = a.argmax[crow[c]];
     else if (fast) sh_left = 1;  // benign race: every writer stores 1
@@ -259,8 +365,11 @@ __device__ void slowfast_commit(const LockArgs& a, int b, int C, const float* cc
   __syncthreads();
   uint64_t* fz = a.frozen + (size_t)b * W;
   if (sh_left) {
-    for (int c = tid; c < C; c += kLockThreads)
-      if (cpos[c] >= hi) atomicOr((unsigned long long*)&fz[cpos[c] >> 6], 1ull << (cpos[c] & 63));
+    for (int c0 = 0; c0 < C; c0 += kLockThreads) {
+      const int c = c0 + tid;
+      const int p = c < C ? cpos[c] : 0;
+      or_position_bits(fz, c < C && p >= hi, p);
+    }
   } else {
     if (tid == 0)
       for (int j = 0; j < kSfStateInts; ++j) st[j] = 0;
@@ -278,12 +387,13 @@ __device__ void slowfast_commit(const LockArgs& a, int b, int C, const float* cc
 }
 
 __global__ __launch_bounds__(kLockThreads) void commit_lock_kernel(LockArgs a) {
-  extern __shared__ unsigned char smem[];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int cap = a.sampler == 1 ? a.N : a.blk_hi - a.blk_lo;
-  float* cconf = reinterpret_cast<float*>(smem);
-  int* cpos = reinterpret_cast<int*>(cconf + (cap > 0 ? cap : 1));
-  int* crow = cpos + (cap > 0 ? cap : 1);
-  __shared__ int ncand;
+  const int cap16 = ((cap > 0 ? cap : 1) + 15) & ~15;  // arrays padded to 16
+  uint64_t* ckey = reinterpret_cast<uint64_t*>(smem);
+  float* cconf = reinterpret_cast<float*>(ckey + cap16);
+  int* cpos = reinterpret_cast<int*>(cconf + cap16);
+  int* crow = cpos + cap16;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int N = a.N, W = (N + 63) >> 6;
   const int r0 = a.row_start[b], r1 = a.row_start[b + 1];
@@ -294,63 +404,59 @@ __global__ __launch_bounds__(kLockThreads) void commit_lock_kernel(LockArgs a) {
 
   if (a.do_commit && a.sampler == 1) {
     __shared__ int s_front, e_max;
+    const int C = gather_candidates(
+        a, r0, r1, [&](int pos) { return tok[pos] == a.mask_id; }, cap, ckey, cconf, cpos,
+        crow);
+    // frontier (smallest candidate position) and end point (largest
+    // candidate position with conf >= tau_conv, -1 if none): wave
+    // reductions, then one shared update per wave
     if (tid == 0) {
-      ncand = 0;
       s_front = 0x7fffffff;
       e_max = -1;
     }
     __syncthreads();
-    for (int r = r0 + tid; r < r1; r += kLockThreads) {
-      const int pos = a.row_pos[r];
-      if (tok[pos] == a.mask_id) {
-        const int slot = atomicAdd(&ncand, 1);
-        const float cf = a.conf[r];
-        cconf[slot] = cf;
-        cpos[slot] = pos;
-        crow[slot] = r;
-        atomicMin(&s_front, pos);
-        if (cf >= a.sf_tau_conv) atomicMax(&e_max, pos);
-      }
+    int lo = 0x7fffffff, hi = -1;
+    for (int c = tid; c < C; c += kLockThreads) {
+      lo = min(lo, cpos[c]);
+      if (cconf[c] >= a.sf_tau_conv) hi = max(hi, cpos[c]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      lo = min(lo, __shfl_xor(lo, o));
+      hi = max(hi, __shfl_xor(hi, o));
+    }
+    if ((tid & 63) == 0) {
+      atomicMin(&s_front, lo);
+      atomicMax(&e_max, hi);
     }
     __syncthreads();
-    if (ncand > 0) slowfast_commit(a, b, ncand, cconf, cpos, crow, s_front, e_max);
+    if (C > 0) slowfast_commit(a, b, C, ckey, cconf, cpos, crow, s_front, e_max);
     __syncthreads();
   } else if (a.do_commit && a.k > 0 && cap > 0) {
-    if (tid == 0) ncand = 0;
-    __syncthreads();
-    for (int r = r0 + tid; r < r1; r += kLockThreads) {
-      const int pos = a.row_pos[r];
-      if (pos >= a.blk_lo && pos < a.blk_hi && tok[pos] == a.mask_id) {
-        const int slot = atomicAdd(&ncand, 1);
-        cconf[slot] = a.conf[r];
-        cpos[slot] = pos;
-        crow[slot] = r;
-      }
-    }
-    __syncthreads();
-    const int C = ncand;
-    for (int c = tid; c < C; c += kLockThreads) {
-      const float cf = cconf[c];
-      const int cp = cpos[c];
-      int rank = 0;
-#pragma unroll 8
-      for (int j = 0; j < C; ++j) {
-        const float f = cconf[j];
-        rank += (f > cf) || (f == cf && cpos[j] < cp);
-      }
-      if (rank < a.k) tok[cp] = a.argmax[crow[c]];
-    }
+    const int C = gather_candidates(
+        a, r0, r1,
+        [&](int pos) { return pos >= a.blk_lo && pos < a.blk_hi && tok[pos] == a.mask_id; },
+        cap, ckey, cconf, cpos, crow);
+    for (int c = tid; c < C; c += kLockThreads)
+      if (rank_upto(c, C, ckey, a.k, [](int) { return true; }) < a.k)
+        tok[cpos[c]] = a.argmax[crow[c]];
   }
   if (a.do_lock && a.policy == 1) {
     uint64_t* bw = a.bits + (size_t)b * W;
-    for (int r = r0 + tid; r < r1; r += kLockThreads) {
-      const int pos = a.row_pos[r];
-      const bool pass = a.row_real[r] && a.has_kl[r] && (a.kl[r] <= a.kl_eps) &&
-                        (a.conf[r] >= a.conf_tau);
-      int32_t* cnt = a.counters + (size_t)b * N + pos;
-      const int c = pass ? *cnt + 1 : 0;
-      *cnt = c;
-      if (c >= a.n_consec) atomicOr((unsigned long long*)&bw[pos >> 6], 1ull << (pos & 63));
+    for (int c0 = r0; c0 < r1; c0 += kLockThreads) {
+      const int r = c0 + tid;
+      int pos = 0;
+      bool lock = false;
+      if (r < r1) {
+        pos = a.row_pos[r];
+        const bool pass = a.row_real[r] && a.has_kl[r] && (a.kl[r] <= a.kl_eps) &&
+                          (a.conf[r] >= a.conf_tau);
+        int32_t* cnt = a.counters + (size_t)b * N + pos;
+        const int c = pass ? *cnt + 1 : 0;
+        *cnt = c;
+        lock = c >= a.n_consec;
+      }
+      or_position_bits(bw, lock, pos);
     }
     if (a.lock_prompt) {
       for (int wd = tid; wd * 64 < a.P; wd += kLockThreads) {
@@ -364,7 +470,11 @@ __global__ __launch_bounds__(kLockThreads) void commit_lock_kernel(LockArgs a) {
 
 hipError_t launch_commit_lock(const LockArgs& a, hipStream_t s) {
   const int cap = std::max(1, a.sampler == 1 ? a.N : a.blk_hi - a.blk_lo);
-  const size_t lds = (size_t)cap * (sizeof(float) + 2 * sizeof(int));
+  const size_t lds =
+      (size_t)((cap + 15) & ~15) * (sizeof(uint64_t) + sizeof(float) + 2 * sizeof(int));
+  if (lds > 64 * 1024)
+    (void)hipFuncSetAttribute((const void*)commit_lock_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   commit_lock_kernel<<<a.B, kLockThreads, lds, s>>>(a);
   return hipGetLastError();
 }

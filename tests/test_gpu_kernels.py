@@ -508,11 +508,18 @@ def test_commit_lock_golden(case):
     assert cnt.tolist() == case["expect_cnt"]
 
 
-@pytest.mark.parametrize("seed", range(6))
+# (batch, seq_len, prompt_len, steps, block_len): blocks of 130 (one gather
+# pass per sequence); blocks of 1250 with more than 1024 rows per sequence
+# (several gather passes) and k of about 60 or 400 per step
+COMMIT_RUNS = [(3, 300, 40, 20, 130)] * 6 + [(2, 2600, 100, 40, 1250)] * 2 + \
+    [(2, 2600, 100, 6, 1250)] * 2
+
+
+@pytest.mark.parametrize("seed", range(len(COMMIT_RUNS)))
 def test_commit_lock_random_vs_oracle(seed):
     rng = np.random.default_rng(100 + seed)
-    B, N, P = 3, 300, 40
-    run = synth.RunShape(B, N, P, 20, 130)
+    B, N, P, T, blk = COMMIT_RUNS[seed]
+    run = synth.RunShape(B, N, P, T, blk)
     V = 50
     lock = dict(policy="test", kl_eps=1e-3, conf_tau=0.3, n_consec=2,
                 lock_prompt_after_first_step=1)
