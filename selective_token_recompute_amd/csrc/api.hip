@@ -491,7 +491,7 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out) {
     // small pass merges them per row.
     GemmArgs g{dt, kEpiLogitsStats, M, V, d, a, h->lm, nullptr, zc, row_seq, row_pos, N,
                m.mask_id, nullptr, nullptr, nullptr, nullptr, 0, 0, h->at<float>(y.z[prv]),
-               h->at<float>(y.lse[prv]), h->at<int32_t>(y.has_prev), ws};
+               h->at<float>(y.lse[prv]), h->at<int32_t>(y.has_prev), ws, r.kl_dir};
     const double fl = 2.0 * M * (double)V * d;
     const double by = V * (double)d * es + M * (double)d * es + M * (double)V * 8.0;
     h->flops += fl;
@@ -1093,7 +1093,8 @@ int dlm_op_lm_head_stats(int32_t M, int32_t V, int32_t K, const void* A, const v
   if ((size_t)M * nparts * kVocabPartBytes > ws_bytes) return DLM_E_SIZE;
   hipStream_t s = (hipStream_t)stream;
   GemmArgs g{kBF16, kEpiLogitsStats, M, V, K, A, W, nullptr, z_cur, row_seq, row_pos, seq_len,
-             mask_id, nullptr, nullptr, nullptr, nullptr, 0, 0, z_prev, lse_prev, has_prev, ws};
+             mask_id, nullptr, nullptr, nullptr, nullptr, 0, 0, z_prev, lse_prev, has_prev, ws,
+             kl_dir};
   const hipError_t e = launch_gemm_logits_stats(g, cfg, s);
   if (e != hipSuccess) return e == hipErrorInvalidValue ? DLM_E_UNSUPPORTED : DLM_E_HIP;
   return hip_status(launch_vocab_merge_parts(M, nparts, seq_len, kl_dir, row_seq, row_pos,

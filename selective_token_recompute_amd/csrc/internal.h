@@ -63,12 +63,13 @@ struct GemmArgs {
   int nq, nkv;
   // kEpiLogitsStats only: previous-step logits [B][seq_len][N] and
   // log-normaliser [B][seq_len], has_prev [B][seq_len] (read only), the
-  // partials out [M][gemm_logits_stats_parts()] (VocabPart; S1 and T1 both
-  // accumulated, so either KL direction can be finished from them).
+  // partials out [M][gemm_logits_stats_parts()] (VocabPart; S1 accumulated
+  // for kl_dir 0, T1 for kl_dir 1: the sums that direction's KL needs).
   const float* zprev;
   const float* lse_prev;
   const int32_t* has_prev;
   void* parts;
+  int kl_dir = 0;
 };
 size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K);
 hipError_t launch_gemm(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s);

@@ -44,6 +44,7 @@ struct EpiParams {
   const float* lse_prev;
   const int32_t* has_prev;
   VocabPart* parts;
+  int kl_dir;
 };
 
 template <int EPI, typename T>
@@ -174,10 +175,22 @@ __device__ __forceinline__ void static_for(F& f) {
 // accumulators over AGPRs and VGPRs and copies them between the two files
 // every iteration; with it, they stay in VGPRs (252 on the 96x192 tile, no
 // spills).
+// Two waves per SIMD (at most 256 registers each) for the 4-wave prefetch
+// tiles, and for the 4-wave statistics tiles whose LDS ring lets two
+// workgroups share a CU (one's epilogue then overlaps the other's main loop).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI, bool PF>
+constexpr int gemm_waves_per_simd() {
+  return (WAVES_M * WAVES_N == 4 &&
+          (PF || (EPI == kEpiLogitsStats && STAGES * (BM + BN) * BK * 2 <= 80 * 1024)))
+             ? 2
+             : 1;
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI, bool SPLIT,
           bool PF = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
-                             (PF && WAVES_M * WAVES_N == 4) ? 2 : 1) void gemm_bf16_mfma_kernel(
+                             (gemm_waves_per_simd<BM, BN, WAVES_M, WAVES_N, STAGES, BK, EPI,
+                                                  PF>())) void gemm_bf16_mfma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, const bf16_t* __restrict__ W2,
     EpiParams ep, int K, int k_per_split, int tiles_m, int tiles_n, float* __restrict__ partial) {
   constexpr bool DUAL = EPI == kEpiSwiglu;
@@ -550,8 +563,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
     // one row block (16 rows) of the wave per call, expanded at compile time
     // (a plain unrolled loop over the row blocks exceeds the unroller's size
     // limit for the largest tiles, which would leave acc in scratch)
-    auto row_block = [&](auto I) __attribute__((always_inline)) {
+    auto row_block = [&](auto I, auto D) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
+      constexpr int kd = decltype(D)::value;  // KL direction whose sums are folded
       float(&cur)[4][TN] = pick<(i & 1) != 0>(zpa, zpb);
       float(&nxt)[4][TN] = pick<(i & 1) == 0>(zpa, zpb);
       if constexpr (i + 1 < TM) load_block(std::integral_constant<int, i + 1>{}, nxt);
@@ -569,7 +583,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
           if (col < N) {
             const float zv = (col == ep.mask_id) ? -INFINITY : acc[i][j][q];
             if (row < M) zrow[col] = zv;
-            vpart_visit<2>(a, col, zv, cur[q][j], hp, mt.lsep, ep.mask_id);
+            vpart_visit<kd>(a, col, zv, cur[q][j], hp, mt.lsep, ep.mask_id);
           }
         }
 #pragma unroll
@@ -580,7 +594,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
       // (register pressure of the large tiles)
       asm volatile("" ::: "memory");
     };
-    static_for<TM>(row_block);
+    // one instance per KL direction: the reverse direction's extra
+    // exponential per logit is spent only when it is asked for
+    auto rows_fwd = [&](auto I) __attribute__((always_inline)) {
+      row_block(I, std::integral_constant<int, 0>{});
+    };
+    auto rows_rev = [&](auto I) __attribute__((always_inline)) {
+      row_block(I, std::integral_constant<int, 1>{});
+    };
+    if (ep.kl_dir == 0)
+      static_for<TM>(rows_fwd);
+    else
+      static_for<TM>(rows_rev);
     __syncthreads();
     for (int t = tid; t < BM; t += 64 * NW) {
       const int row = m0 + t;
@@ -1027,7 +1052,7 @@ hipError_t dispatch_generic(const GemmArgs& a, EpiParams ep, hipStream_t s) {
 EpiParams epi_params(const GemmArgs& a) {
   return EpiParams{a.C,  a.M,   a.N,  a.row_seq, a.row_pos, a.seq_len,  a.mask_id,
                    a.rope, (bf16_t*)a.q, (bf16_t*)a.kc, (bf16_t*)a.vc, a.nq, a.nkv,
-                   a.zprev, a.lse_prev, a.has_prev, (VocabPart*)a.parts};
+                   a.zprev, a.lse_prev, a.has_prev, (VocabPart*)a.parts, a.kl_dir};
 }
 
 hipError_t launch_plan(const GemmArgs& a, Plan p, void* ws, size_t ws_bytes, hipStream_t s) {
