@@ -168,3 +168,31 @@ def test_checkpoint_refusals():
     other.lock_update()
     for e in (e1, other):
         e.close()
+
+
+def test_resume_at_the_llada_shape():
+    """Full LLaDA-8B shape (32 layers, d = 4096, V = 126464, N = 512; the image
+    holds 259 MB of previous logits and 268 MB of K/V): saved after 3 scheduled
+    steps into device memory, resumed in a fresh handle; the next 3 steps
+    (M from 381 down, on the fused LM-head statistics path) are bitwise those
+    of the uninterrupted run."""
+    shape, run = synth.CONFIGS["llada8b"]
+    lock = synth.LOCK_SETTINGS["scheduled"]
+    dw = E.random_device_weights(shape, seed=0)
+    pr = torch.from_numpy(synth.gen_prompts(shape, run)).cuda()
+    e1 = E.Engine(shape, dw, run, lock, pr)
+    for _ in range(3):
+        e1.step()
+        e1.lock_update()
+    img = torch.empty(e1.checkpoint_bytes(), dtype=torch.uint8, device="cuda")
+    assert img.numel() > 500_000_000
+    e1.save_checkpoint(img)
+    ref = _run_to_end(e1, 3, 6)
+    e1.close()
+    e2 = E.Engine(shape, dw, run, lock, pr)
+    e2.load_checkpoint(img)
+    got = _run_to_end(e2, 3, 6)
+    for i, ((rm, ru), (gm, gu)) in enumerate(zip(ref, got)):
+        _assert_same(rm, gm, f"step {3 + i} (posterior)")
+        _assert_same(ru, gu, f"step {3 + i} (update)")
+    e2.close()
