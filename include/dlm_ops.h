@@ -212,9 +212,9 @@ int dlm_op_vocab_stats(int32_t M, int32_t V, int32_t mask_id, int32_t kl_dir, in
  * per-position outputs as dlm_op_vocab_stats (SureLock page, §2 locking
  * condition) without re-reading z_cur: each output tile folds its logits and
  * the row's previous logits into online partial sums (maximum, sum of
- * e^{z-max}, sum of e^{z-max}(z - z_prev), sum of q(z_prev - z)), one
- * partial per row and column tile in ws, which a second kernel merges per
- * row.  ws: at least dlm_op_lm_head_stats_ws_bytes(M, V, K, cfg) bytes of
+ * e^{z-max}, and the sum the requested KL direction needs: e^{z-max}(z -
+ * z_prev) for kl_dir 0, q(z_prev - z) for kl_dir 1), one partial per row and
+ * column tile in ws, which a second kernel merges per row.  ws: at least dlm_op_lm_head_stats_ws_bytes(M, V, K, cfg) bytes of
  * device memory (no initial contents needed).  cfg: -1 for the default tile
  * plan, else a tile configuration index (tuning; DLM_E_UNSUPPORTED for a
  * configuration the fused epilogue is not built for). */
