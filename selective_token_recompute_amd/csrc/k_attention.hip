@@ -966,6 +966,7 @@ struct AttnPlan {
 };
 
 constexpr size_t kAttnSplitCap = 64ull << 20;  // split-KV partials never exceed this
+constexpr int kAttnCUs = 256;                    // compute units of an MI355X
 
 // Splits the keys while fewer than 128 workgroups would be busy (the
 // combine pass costs a launch plus a write and a read of every partial
@@ -1150,12 +1151,24 @@ A32Plan make_a32_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd, i
   // query vectors per (sequence, kv head), the rows spread evenly
   const int qph = (M * G + B - 1) / B;
   if (lay < 0 || lay >= kNumA32) {
-    // measured best: 128 queries per workgroup from ~768 per head, 64 from
-    // ~320, 32 between 64 and 320, and 64 below (one workgroup per head)
-    if (qph >= 768) lay = 2;
-    else if (qph >= 320) lay = 1;
-    else if (qph > 64) lay = 0;
-    else lay = 1;
+    // 64 queries per workgroup up to 64 per head (one workgroup per head,
+    // 8 waves); above, the smallest query tile (32, 64, 128) whose
+    // workgroups all run in one round: each holds 128 KB of LDS, so one per
+    // CU, and a grid one round too large ran 1.5-1.7x slower (N = 512,
+    // M = 264..300: 21.3 against 12.5 us with 64 queries; N = 1024,
+    // M = 544..736: 34-36 against 23-24 us with 128)
+    if (qph <= 64) {
+      lay = 1;
+    } else {
+      lay = 2;
+      for (int c : {0, 1}) {
+        const int qt = 32 * kA32[c].qw * kA32[c].qb;
+        if ((long long)B * nkv * ((qph + qt - 1) / qt) <= kAttnCUs) {
+          lay = c;
+          break;
+        }
+      }
+    }
   }
   const A32Layout& L = kA32[lay];
   if (N % L.kt) {
@@ -1176,7 +1189,7 @@ A32Plan make_a32_plan(int dtype, int M, int B, int N, int nq, int nkv, int hd, i
     // splitting the keys (partials merged by the combine pass) paid only
     // from N = 1024, with few busy workgroups and at least two tiles per
     // range: M = 20 (32 workgroups) 4 ranges, M = 102 (128) 2 ranges
-    while (N >= 1024 && busy * splits * 2 <= 256 && ktiles / (splits * 2) >= 2 &&
+    while (N >= 1024 && busy * splits * 2 <= kAttnCUs && ktiles / (splits * 2) >= 2 &&
            ws_of(splits * 2) <= kAttnSplitCap)
       splits *= 2;
   }

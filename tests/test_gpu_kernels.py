@@ -234,6 +234,8 @@ def test_attention_32x32_layouts(layout, splits, hd):
     (1, 512, 32, 32, [384]),    # the LLaDA-8B step at M = 384
     (1, 1024, 32, 32, [20]),    # one layer over a 1024-key cache at M = 20 (key splits)
     (1, 512, 32, 32, [9]),      # the end of a scheduled-lock run
+    (1, 512, 32, 32, [288]),    # 64-query tiles: 32-query ones would need two rounds of CUs
+    (1, 1024, 32, 32, [640]),   # 128-query tiles, for the same reason
     (2, 1024, 28, 4, [700, 1]),  # Dream-7B grouping, uneven sequences
 ])
 def test_attention_32x32_default_plan(B, N, nq, nkv, rows):
