@@ -888,8 +888,36 @@ Plan make_plan_cfg(int dtype, int epi, int M, int N, int K, int cfg) {
   return p;
 }
 
+// Large-M plans of the single-output GEMMs pick the 8-wave 256x256 tile,
+// one workgroup per CU.  When that grid does not split K and its last round
+// of workgroups leaves many CUs idle (the Dream-7B projections, N = 3584:
+// 14 column tiles, so 336 workgroups at M = 6144, 1.31 rounds), the 12-wave
+// 256x192 tile is taken instead if it scores higher on fill (workgroups over
+// the CU slots of the rounds they need) per byte pulled per FLOP (1/bm +
+// 1/bn).  Measured there with the weights cold: O 228.8 -> 181.6 us, down
+// 980 -> 864 us at M = 6144; at M = 3792 (210 workgroups, one round) the
+// 256x256 tile stays ahead and is kept.
+int refine_wide_cfg(int cfg, int M, int N) {
+  constexpr int kWideTile = 13, kWideAlt = 50;
+  if (cfg != kWideTile) return cfg;
+  auto grid = [&](int c) {
+    return ((M + kCfgs[c].bm - 1) / kCfgs[c].bm) * ((N + kCfgs[c].bn - 1) / kCfgs[c].bn);
+  };
+  const int t13 = grid(kWideTile);
+  if (t13 * 2 <= kCUs) return cfg;  // the plan splits K to fill the CUs
+  auto score = [&](int c) {
+    const int w = grid(c);
+    const double fill = (double)w / (((w + kCUs - 1) / kCUs) * kCUs);
+    return fill / (1.0 / kCfgs[c].bm + 1.0 / kCfgs[c].bn);
+  };
+  return score(kWideAlt) > score(kWideTile) ? kWideAlt : kWideTile;
+}
+
 Plan make_plan(int dtype, int epi, int M, int N, int K) {
-  return make_plan_cfg(dtype, epi, M, N, K, pick_cfg(M, N, K, epi == kEpiSwiglu));
+  const bool dual = epi == kEpiSwiglu;
+  int cfg = pick_cfg(M, N, K, dual);
+  if (!dual) cfg = refine_wide_cfg(cfg, M, N);
+  return make_plan_cfg(dtype, epi, M, N, K, cfg);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK, int EPI, bool PF = false>

@@ -68,7 +68,10 @@ def test_gemm_store_bf16_ragged_m(M):
 
 
 @pytest.mark.parametrize("M,N,K", [(7, 200, 128), (130, 72, 256), (512, 4096, 4096),
-                                   (384, 12288, 128), (9, 4096, 12288)])
+                                   (384, 12288, 128), (9, 4096, 12288),
+                                   # Dream-7B width at large M: the plan trades the
+                                   # 256x256 tile for 256x192 to fill the last round
+                                   (2500, 3584, 256)])
 def test_gemm_resid_add_bf16(M, N, K):
     A, W, _ = _gemm_inputs(M, N, K, seed=N + K)
     h0 = synth.gen_normal((M, N), 99, 1.0)
