@@ -897,20 +897,25 @@ Plan make_plan_cfg(int dtype, int epi, int M, int N, int K, int cfg) {
 // 1/bn).  Measured there with the weights cold: O 228.8 -> 181.6 us, down
 // 980 -> 864 us at M = 6144; at M = 3792 (210 workgroups, one round) the
 // 256x256 tile stays ahead and is kept.
+int tile_grid(int c, int M, int N) {
+  return ((M + kCfgs[c].bm - 1) / kCfgs[c].bm) * ((N + kCfgs[c].bn - 1) / kCfgs[c].bn);
+}
+
+// Fill of the rounds a grid of tile c needs (its workgroups over the
+// resident slots of those rounds) per byte pulled into the CUs per FLOP
+// (1/bm + 1/bn): larger is better.
+double fill_score(int c, int M, int N) {
+  const int slots = kCUs * (cfg_lds(kCfgs[c]) <= 80 * 1024 ? 2 : 1);
+  const int w = tile_grid(c, M, N);
+  const double fill = (double)w / (((w + slots - 1) / slots) * slots);
+  return fill / (1.0 / kCfgs[c].bm + 1.0 / kCfgs[c].bn);
+}
+
 int refine_wide_cfg(int cfg, int M, int N) {
   constexpr int kWideTile = 13, kWideAlt = 50;
   if (cfg != kWideTile) return cfg;
-  auto grid = [&](int c) {
-    return ((M + kCfgs[c].bm - 1) / kCfgs[c].bm) * ((N + kCfgs[c].bn - 1) / kCfgs[c].bn);
-  };
-  const int t13 = grid(kWideTile);
-  if (t13 * 2 <= kCUs) return cfg;  // the plan splits K to fill the CUs
-  auto score = [&](int c) {
-    const int w = grid(c);
-    const double fill = (double)w / (((w + kCUs - 1) / kCUs) * kCUs);
-    return fill / (1.0 / kCfgs[c].bm + 1.0 / kCfgs[c].bn);
-  };
-  return score(kWideAlt) > score(kWideTile) ? kWideAlt : kWideTile;
+  if (tile_grid(kWideTile, M, N) * 2 <= kCUs) return cfg;  // the plan splits K to fill the CUs
+  return fill_score(kWideAlt, M, N) > fill_score(kWideTile, M, N) ? kWideAlt : kWideTile;
 }
 
 Plan make_plan(int dtype, int epi, int M, int N, int K) {
@@ -1124,19 +1129,31 @@ bool gemm_qkv_fusable(int dtype, int M, int hd, int K) {
 // 192, but run each tile less efficiently (4 waves, or 48-column wave tiles),
 // so they gain only 2-9%; 64-column (half-head) tiles stream the weights with
 // twice the workgroups at M <= 64 (13-22% faster there).
-int pick_qkv_cfg(int M) {
+int pick_qkv_cfg(int M, int N) {
   if (M <= 32) return 7;    // 32x64, 4 waves: weight streaming, 192 half-head column tiles
   if (M <= 64) return 14;   // 64x64
   if (M <= 128) return 1;   // 64x128
   if (M <= 192) return 6;   // 96x128
   if (M <= 256) return 8;   // 128x128, 8 waves
   if (M <= 384) return 45;  // 96x192, 12 waves, prefetch: 8-12% ahead of 4 waves
-  return 42;                // 128x192, 8 waves, fragment prefetch
+  if (M <= 512) return 42;  // 128x192, 8 waves, fragment prefetch
+  // Larger M: the tile with the best fill per byte (fill_score) among the
+  // 128x192, 96x192, 12-wave 192x192, 12-wave 256x192 and 128x128 tiles (the
+  // first on ties).  Against the weights cold, that rule picked the fastest
+  // tile, or one within 2% of it, at every point measured: the LLaDA-8B
+  // width (12288 columns) at M = 768 .. 12288 and the Dream-7B width (4608)
+  // at M = 700 .. 6144, where the 128x192 tile alone ran up to 1.4x slower
+  // (Dream-7B at M = 1392: 85.7 against 59.9 us).
+  static const int kCand[] = {42, 45, 46, 50, 8};
+  int best = kCand[0];
+  for (int c : kCand)
+    if (fill_score(c, M, N) > fill_score(best, M, N)) best = c;
+  return best;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
   if (a.epi == kEpiQKV)
-    return launch_plan(a, make_plan_cfg(a.dtype, a.epi, a.M, a.N, a.K, pick_qkv_cfg(a.M)), ws,
+    return launch_plan(a, make_plan_cfg(a.dtype, a.epi, a.M, a.N, a.K, pick_qkv_cfg(a.M, a.N)), ws,
                        ws_bytes, s);
   return launch_plan(a, make_plan(a.dtype, a.epi, a.M, a.N, a.K), ws, ws_bytes, s);
 }
