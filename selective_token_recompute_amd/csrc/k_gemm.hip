@@ -918,10 +918,26 @@ int refine_wide_cfg(int cfg, int M, int N) {
   return fill_score(kWideAlt, M, N) > fill_score(kWideTile, M, N) ? kWideAlt : kWideTile;
 }
 
+// gate/up + SwiGLU above M = 384: the tile with the best fill_score over
+// the 2 d_ff output columns among 256x192, 256x256 and the 12-wave 192x192
+// (the first on ties).  Swept with the weights cold it picked the fastest
+// tile at every point at the LLaDA-8B width (M = 512 .. 4096; M = 768: 130
+// against 172 us for 256x192) and the Dream-7B width (M = 700 .. 6144;
+// M = 700: 185 against 233 us).  At M <= 384 the table from the engine A/Bs
+// stands.
+int pick_dual_cfg(int cfg, int M, int N) {
+  if (M <= 384) return cfg;
+  static const int kCand[] = {50, 13, 46};
+  int best = kCand[0];
+  for (int c : kCand)
+    if (fill_score(c, M, 2 * N) > fill_score(best, M, 2 * N)) best = c;
+  return best;
+}
+
 Plan make_plan(int dtype, int epi, int M, int N, int K) {
   const bool dual = epi == kEpiSwiglu;
   int cfg = pick_cfg(M, N, K, dual);
-  if (!dual) cfg = refine_wide_cfg(cfg, M, N);
+  cfg = dual ? pick_dual_cfg(cfg, M, N) : refine_wide_cfg(cfg, M, N);
   return make_plan_cfg(dtype, epi, M, N, K, cfg);
 }
 

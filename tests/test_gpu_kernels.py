@@ -86,7 +86,10 @@ def test_gemm_resid_add_bf16(M, N, K):
                                    (100, 320, 512), (384, 320, 512),
                                    # the 12-wave 256x192 tile of 384 < M <= 1536 at the
                                    # model's K: ragged M, several k-slices
-                                   (385, 384, 4096), (700, 384, 4096), (1536, 384, 4096)])
+                                   (385, 384, 4096), (700, 384, 4096), (1536, 384, 4096),
+                                   # the fill-per-byte choice above M = 384: the 12-wave
+                                   # 192x192 tile at d_ff 12288, 256x256 at d_ff 18944
+                                   (640, 12288, 256), (640, 18944, 128)])
 def test_gemm_swiglu_bf16(M, N, K):
     A, Wg, Wu = _gemm_inputs(M, N, K, seed=7 * M)
     U = ops.gemm(L.DLM_EPI_SWIGLU, _dev(A), _dev(Wg), W2=_dev(Wu))
