@@ -350,6 +350,25 @@ def test_slowfast_lockstep_bf16_two_sequences():
     assert rep["replays"] <= rep["ambiguous"], rep
 
 
+@pytest.mark.timeout(1500)
+def test_slowfast_lockstep_depth32():
+    """The SlowFast sampler at the LLaDA-8B run shape and depth (one sequence
+    of 512, 128 prompt + 384 masked, 128 steps, 32 bf16 layers at d = 256):
+    the whole run in lockstep with the oracle, with the engineered setting
+    above so that spans stop short, positions freeze and return, and cycles
+    restart; decisions bit for bit after replay of ambiguous steps only."""
+    from tests.test_gpu_depth import DEPTH32, RUN
+    W = synth.gen_weights(DEPTH32)
+    pr = synth.gen_prompts(DEPTH32, RUN)
+    lock, e = _engineered_lock(W, DEPTH32, RUN, pr, sf_k=3, sf_kmax=8)
+    rep = run_slowfast_lockstep(DEPTH32, W, RUN, lock, pr)
+    print(f"\n[slowfast depth32] end point {e} {rep}")
+    append_record(dict(name="slowfast/depth32", **rep))
+    assert rep["steps"] == RUN.steps and rep["cycles"] > 0
+    assert rep["frozen_steps"] > 0 and rep["returns"] > 0
+    assert rep["replays"] <= rep["ambiguous"], rep
+
+
 def test_slowfast_llada_full_shape_invariants():
     """The bench's slowfast setting at the full LLaDA-8B shape: decoded and
     locked tokens never change, the frozen set holds only masked positions
