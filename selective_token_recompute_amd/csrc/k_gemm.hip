@@ -652,6 +652,31 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
             if (row < M) epi_store<EPI, bf16_t>(ep, row, col, acc[i][j][q], acc[i][j + TN / 2][q]);
           }
         }
+      } else if constexpr (EPI == kEpiResidAdd) {
+        // h += acc: the row block's loads first, then the adds and stores
+        // (element by element, every load would wait for the store before
+        // it, which may alias as far as the compiler can tell)
+        float* C = (float*)ep.C;
+        float hv[TN][4];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + brow(j) + cl;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = m0 + wm * WM + i * 16 + rq + q;
+            hv[j][q] = (col < N && row < M) ? C[(size_t)row * N + col] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + brow(j) + cl;
+          if (col >= N) continue;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = m0 + wm * WM + i * 16 + rq + q;
+            if (row < M) C[(size_t)row * N + col] = hv[j][q] + acc[i][j][q];
+          }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
