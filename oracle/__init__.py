@@ -67,7 +67,8 @@ class _Run(ctypes.Structure):
                 ("policy", ctypes.c_int32), ("sampler", ctypes.c_int32),
                 ("sf_k", ctypes.c_int32), ("sf_kmax", ctypes.c_int32),
                 ("sf_whist", ctypes.c_int32), ("sf_tau_conv", ctypes.c_double),
-                ("sf_tau_high", ctypes.c_double), ("sf_var", ctypes.c_double)]
+                ("sf_tau_high", ctypes.c_double), ("sf_var", ctypes.c_double),
+                ("refresh_budget", ctypes.c_int32), ("refresh_eps", ctypes.c_double)]
 
 
 _PF = ctypes.POINTER(ctypes.c_float)
@@ -104,7 +105,7 @@ def lib():
         L.orc_flops.argtypes = [vp]
         L.orc_flops.restype = ctypes.c_double
         for f in ("orc_get_tokens", "orc_get_locked", "orc_get_cnt", "orc_get_frozen",
-                  "orc_get_sf", "orc_get_has_prev"):
+                  "orc_get_sf", "orc_get_has_prev", "orc_get_drift", "orc_get_refresh"):
             getattr(L, f).argtypes = [vp, vp]
         L.orc_get_rows.argtypes = [vp, vp, vp, vp]
         L.orc_get_stats.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -122,7 +123,8 @@ def lib():
                                            ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
         L.orc_unit_schedule.argtypes = [ctypes.POINTER(_Run), ctypes.c_int, vp]
         L.orc_unit_lock_transition.argtypes = [ctypes.POINTER(_Model), ctypes.POINTER(_Run),
-                                               ctypes.c_int, ctypes.c_int] + [vp] * 10
+                                               ctypes.c_int, ctypes.c_int] + [vp] * 12
+        L.orc_unit_refresh_select.argtypes = [ctypes.POINTER(_Run), vp, vp, vp]
         L.orc_unit_compact.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.orc_unit_slowfast.argtypes = [ctypes.POINTER(_Run)] + [ctypes.c_int] * 3 + [vp] * 9
         L.orc_num_threads.restype = ctypes.c_int
@@ -153,7 +155,9 @@ def make_run(run, lock: Dict) -> _Run:
                 float(lock["kl_eps"]), float(lock["conf_tau"]), int(lock["n_consec"]),
                 int(lock.get("kl_dir", 0)), int(lock["lock_prompt_after_first_step"]),
                 POLICY[lock["policy"]], SAMPLER[lock.get("sampler", "semi_ar")],
-                *[type(v)(lock.get(k, v)) for k, v in SF_DEFAULTS.items()])
+                *[type(v)(lock.get(k, v)) for k, v in SF_DEFAULTS.items()],
+                int(lock.get("refresh_budget", 0)),
+                float(lock.get("refresh_eps", lock["kl_eps"])))
 
 
 def num_threads() -> int:
@@ -271,6 +275,19 @@ class Oracle:
         """uint8 [B][N]: a previous-step posterior is stored."""
         out = np.empty(self._bn(), dtype=np.uint8)
         lib().orc_get_has_prev(self._h, _ptr(out))
+        return out
+
+    def drift(self) -> np.ndarray:
+        """float32 [B][N]: each position's KL between its two latest
+        posteriors (+inf while undefined)."""
+        out = np.empty(self._bn(), dtype=np.float32)
+        lib().orc_get_drift(self._h, _ptr(out))
+        return out
+
+    def refresh(self) -> np.ndarray:
+        """uint8 [B][N]: locked positions the last step recomputed."""
+        out = np.empty(self._bn(), dtype=np.uint8)
+        lib().orc_get_refresh(self._h, _ptr(out))
         return out
 
     def sf_state(self) -> np.ndarray:
@@ -395,7 +412,10 @@ def unit_schedule(run, t: int):
 
 
 def unit_lock_transition(shape, run, lock, t, row_seq, row_pos, row_real, argmax, conf, kl,
-                         has_kl, x, locked, cnt):
+                         has_kl, x, locked, cnt, refresh=None, drift=None):
+    """Commit + lock transition on given statistics.  refresh: optional
+    uint8 [B][N] set of locked positions the step recomputed; drift: optional
+    float32 [B][N], updated and returned as a fourth value when given."""
     m = make_model(shape)
     r = make_run(run, lock)
     a = [np.ascontiguousarray(row_seq, np.int32), np.ascontiguousarray(row_pos, np.int32),
@@ -404,9 +424,27 @@ def unit_lock_transition(shape, run, lock, t, row_seq, row_pos, row_real, argmax
     x = np.ascontiguousarray(x, np.int32).copy()
     locked = np.ascontiguousarray(locked, np.uint8).copy()
     cnt = np.ascontiguousarray(cnt, np.int32).copy()
+    rf = None if refresh is None else np.ascontiguousarray(refresh, np.uint8)
+    dr = None if drift is None else np.ascontiguousarray(drift, np.float32).copy()
     lib().orc_unit_lock_transition(ctypes.byref(m), ctypes.byref(r), t, len(a[0]),
-                                   *[_ptr(v) for v in a], _ptr(x), _ptr(locked), _ptr(cnt))
+                                   *[_ptr(v) for v in a], _ptr(x), _ptr(locked), _ptr(cnt),
+                                   None if rf is None else _ptr(rf),
+                                   None if dr is None else _ptr(dr))
+    if dr is not None:
+        return x, locked, cnt, dr
     return x, locked, cnt
+
+
+def unit_refresh_select(run, lock, locked, drift) -> np.ndarray:
+    """Refresh set (uint8 [B][N]) of a step from the lock state and each
+    position's drift: per sequence the refresh_budget locked positions with
+    the largest float32 drift, ties to the smaller position."""
+    r = make_run(run, lock)
+    locked = np.ascontiguousarray(locked, np.uint8)
+    drift = np.ascontiguousarray(drift, np.float32)
+    out = np.empty(locked.shape, np.uint8)
+    lib().orc_unit_refresh_select(ctypes.byref(r), _ptr(locked), _ptr(drift), _ptr(out))
+    return out
 
 
 def unit_slowfast(run, lock, mask_id, pos, argmax, conf, x, frozen, has_prev, state):

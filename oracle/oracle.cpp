@@ -36,6 +36,22 @@
 //    positions beyond the span keep their last prediction and cached K/V
 //    (they leave the active set) until the span is decoded.
 //
+//  * Optional drift-aware partial refresh of locked positions, the
+//    Polestar-Cache idea on the Polestar page ("Polestar: Drift-Aware Cache
+//    Calibration and Token Commitment ...", section "Polestar: The Smart
+//    Painter"): instead of keeping every cached position frozen forever, go
+//    back and recompute only the positions whose understanding drifts most,
+//    drift measured as a KL divergence between the position's successive
+//    distributions.  A locked position's drift can only be observed when it
+//    is recomputed, so the reading here is: a position's drift is the KL (in
+//    the run's direction) between its two most recent posteriors, kept as a
+//    float32 number and +inf while undefined; at every step the
+//    refresh_budget locked positions of each sequence with the largest drift
+//    (ties: smaller position) join the active set, their K/V are recomputed
+//    and their new drift measured against the posterior they had when last
+//    computed; one whose new drift exceeds refresh_eps is unlocked (it stays
+//    active until it passes the lock test again), the others stay locked.
+//
 // Arithmetic is fp64.  In bf16-storage mode the values the GPU engine keeps
 // in bf16 are rounded to bf16 at exactly those points (the normalised GEMM
 // inputs, q, the K/V cache, the attention output and the SwiGLU product);
@@ -82,6 +98,11 @@ typedef struct {
   int32_t sampler;
   int32_t sf_k, sf_kmax, sf_whist;
   double sf_tau_conv, sf_tau_high, sf_var;
+  // drift-aware refresh of locked positions (semi-AR sampler only): locked
+  // positions recomputed per sequence per step (0: off) and the drift above
+  // which a recomputed position is unlocked
+  int32_t refresh_budget;
+  double refresh_eps;
 } orc_run;
 
 typedef struct {
@@ -391,6 +412,8 @@ struct orc_state {
   std::vector<double> prevlogp;    // [B][N][V]
   std::vector<uint8_t> frozen;     // [B][N] out of the active set during an accelerated stage
   std::vector<SfSeq> sf;           // [B] SlowFast cycle state
+  std::vector<float> drift;        // [B][N] KL between the two latest posteriors (+inf: none)
+  std::vector<uint8_t> refresh;    // [B][N] locked positions recomputed by the last step
 
   // results of the last step (rows in (b, pos) ascending order)
   bool stepped = false, partial = false;
@@ -414,6 +437,29 @@ size_t kv_index(const orc_state& s, int l, int b, int g, int pos) {
   return ((((size_t)l * r.batch + b) * m.n_kv_heads + g) * r.seq_len + pos) * m.head_dim;
 }
 
+// Refresh set of one step (Polestar page, "The Smart Painter", Polestar-Cache:
+// recompute only where the drift is largest): per sequence, the
+// refresh_budget locked positions with the largest drift, ties to the
+// smaller position; refresh [B][N] is rewritten.
+void refresh_select(const orc_run& r, const uint8_t* locked, const float* drift,
+                    uint8_t* refresh) {
+  const int N = r.seq_len;
+  std::fill(refresh, refresh + (size_t)r.batch * N, 0);
+  if (r.refresh_budget <= 0) return;
+  for (int b = 0; b < r.batch; ++b) {
+    std::vector<int> cand;
+    for (int i = 0; i < N; ++i)
+      if (locked[(size_t)b * N + i]) cand.push_back(i);
+    const float* dr = drift + (size_t)b * N;
+    std::stable_sort(cand.begin(), cand.end(), [&](int a, int c) {
+      if (dr[a] != dr[c]) return dr[a] > dr[c];
+      return a < c;
+    });
+    const int take = std::min<int>(r.refresh_budget, (int)cand.size());
+    for (int j = 0; j < take; ++j) refresh[(size_t)b * N + cand[j]] = 1;
+  }
+}
+
 // The lock state transition for one step: commit, then lock test.
 // Inputs are the rows of the step (ascending (b, pos)) and their statistics.
 void lock_transition(const orc_model& m, const orc_run& r, int t, int M,
@@ -423,7 +469,8 @@ void lock_transition(const orc_model& m, const orc_run& r, int t, int M,
                      std::vector<int32_t>* cseq, std::vector<int32_t>* cpos,
                      std::vector<int32_t>* ctok, bool do_commit = true, bool do_lock = true,
                      SfSeq* sf = nullptr, uint8_t* frozen = nullptr,
-                     uint8_t* has_prev = nullptr) {
+                     uint8_t* has_prev = nullptr, const uint8_t* refresh = nullptr,
+                     float* drift = nullptr) {
   const int N = r.seq_len;
   const bool slowfast = r.sampler == 1;
   const Sched sc = do_commit && !slowfast ? schedule(r, t) : Sched{-1, 0, 0, 0};
@@ -465,12 +512,27 @@ void lock_transition(const orc_model& m, const orc_run& r, int t, int M,
       }
     }
   }
+  // Drift of every recomputed position: its KL between this posterior and
+  // the one before (a statistic, kept whatever decides the lock state).
+  if (drift)
+    for (int i = 0; i < M; ++i)
+      drift[(size_t)row_seq[i] * N + row_pos[i]] =
+          has_kl[i] ? (float)kl[i] : std::numeric_limits<float>::infinity();
   // Lock test: a row with a real input token passes when its KL is defined,
   // at most eps, and its confidence is at least tau; n_consec consecutive
-  // passes lock it for good.
+  // passes lock it.  A locked position recomputed by the refresh instead
+  // stays locked while its drift is defined and at most refresh_eps, and is
+  // unlocked (counter cleared) otherwise.
   if (do_lock && r.policy == 1) {
     for (int i = 0; i < M; ++i) {
       const size_t p = (size_t)row_seq[i] * N + row_pos[i];
+      if (refresh && refresh[p]) {
+        if (!(has_kl[i] && kl[i] <= r.refresh_eps)) {
+          locked[p] = 0;
+          cnt[p] = 0;
+        }
+        continue;
+      }
       const bool pass = row_real[i] && has_kl[i] && kl[i] <= r.kl_eps && conf[i] >= r.conf_tau;
       cnt[p] = pass ? cnt[p] + 1 : 0;
       if (cnt[p] >= r.n_consec) locked[p] = 1;
@@ -493,7 +555,9 @@ orc_state* orc_create(const orc_model* m, const orc_weights* w, const orc_run* r
   if (r->batch <= 0 || r->seq_len <= 0 || r->prompt_len < 0 || r->prompt_len > r->seq_len ||
       r->steps <= 0 || r->block_len <= 0 || m->n_heads % m->n_kv_heads != 0 ||
       m->head_dim % 2 != 0 || (r->sampler != 0 && r->sampler != 1) ||
-      (r->sampler == 1 && (r->sf_k < 1 || r->sf_kmax < 1 || r->sf_whist < 1 || r->sf_whist > 8)))
+      (r->sampler == 1 && (r->sf_k < 1 || r->sf_kmax < 1 || r->sf_whist < 1 || r->sf_whist > 8)) ||
+      r->refresh_budget < 0 || r->refresh_budget > r->seq_len ||
+      (r->refresh_budget > 0 && r->sampler != 0) || std::isnan(r->refresh_eps))
     return nullptr;
   orc_state* s = new orc_state();
   s->m = *m;
@@ -519,6 +583,8 @@ orc_state* orc_create(const orc_model* m, const orc_weights* w, const orc_run* r
   s->has_prev.assign(BN, 0);
   s->frozen.assign(BN, 0);
   s->sf.assign(r->batch, SfSeq{});
+  s->drift.assign(BN, std::numeric_limits<float>::infinity());
+  s->refresh.assign(BN, 0);
   const size_t kvn = (size_t)L * BN * m->n_kv_heads * m->head_dim;
   s->kc.assign(kvn, 0.0);
   s->vc.assign(kvn, 0.0);
@@ -541,13 +607,16 @@ int orc_step_sample(orc_state* s, const int32_t* sample_rows, int n_sample) {
   const int dff = m.d_ff, V = m.vocab, qo = nq * hd, qkv_out = (nq + 2 * nkv) * hd;
 
   // Active set: every unlocked position, ascending ([SL] §2 permanent
-  // deactivation), less the positions a SlowFast accelerated stage froze.
+  // deactivation), less the positions a SlowFast accelerated stage froze,
+  // plus the locked positions the drift-aware refresh recomputes.
   s->row_seq.clear();
   s->row_pos.clear();
   s->row_real.clear();
+  refresh_select(r, s->locked.data(), s->drift.data(), s->refresh.data());
   for (int b = 0; b < r.batch; ++b)
     for (int i = 0; i < N; ++i)
-      if (!s->locked[(size_t)b * N + i] && !s->frozen[(size_t)b * N + i]) {
+      if ((!s->locked[(size_t)b * N + i] || s->refresh[(size_t)b * N + i]) &&
+          !s->frozen[(size_t)b * N + i]) {
         s->row_seq.push_back(b);
         s->row_pos.push_back(i);
         s->row_real.push_back(s->x[(size_t)b * N + i] != m.mask_id);
@@ -693,7 +762,8 @@ int orc_lock_update(orc_state* s, const int32_t* ov_commit_seq, const int32_t* o
                   s->row_argmax.data(), s->row_conf.data(), s->row_kl.data(),
                   s->row_has_kl.data(), s->x.data(), s->locked.data(), s->cnt.data(),
                   &s->commit_seq, &s->commit_pos, &s->commit_tok, !ov_commit, !ov_lock,
-                  s->sf.data(), s->frozen.data(), s->has_prev.data());
+                  s->sf.data(), s->frozen.data(), s->has_prev.data(), s->refresh.data(),
+                  s->drift.data());
   if (ov_commit) {
     s->commit_seq.assign(ov_commit_seq, ov_commit_seq + n_ov_commit);
     s->commit_pos.assign(ov_commit_pos, ov_commit_pos + n_ov_commit);
@@ -703,7 +773,9 @@ int orc_lock_update(orc_state* s, const int32_t* ov_commit_seq, const int32_t* o
   }
   const size_t BN = (size_t)r.batch * r.seq_len;
   if (ov_lock) {
-    for (size_t p = 0; p < BN; ++p) s->locked[p] = s->locked[p] | (ov_locked[p] ? 1 : 0);
+    // the override also decides the refreshed positions: locked iff given
+    for (size_t p = 0; p < BN; ++p)
+      s->locked[p] = (s->refresh[p] ? 0 : s->locked[p]) | (ov_locked[p] ? 1 : 0);
     if (ov_cnt) std::memcpy(s->cnt.data(), ov_cnt, sizeof(int32_t) * BN);
   }
   s->t += 1;
@@ -720,6 +792,12 @@ void orc_get_locked(const orc_state* s, uint8_t* out) { std::copy(s->locked.begi
 void orc_get_cnt(const orc_state* s, int32_t* out) { std::copy(s->cnt.begin(), s->cnt.end(), out); }
 void orc_get_has_prev(const orc_state* s, uint8_t* out) {
   std::copy(s->has_prev.begin(), s->has_prev.end(), out);
+}
+void orc_get_drift(const orc_state* s, float* out) {
+  std::copy(s->drift.begin(), s->drift.end(), out);
+}
+void orc_get_refresh(const orc_state* s, uint8_t* out) {
+  std::copy(s->refresh.begin(), s->refresh.end(), out);
 }
 void orc_get_frozen(const orc_state* s, uint8_t* out) {
   std::copy(s->frozen.begin(), s->frozen.end(), out);
@@ -818,10 +896,17 @@ int orc_unit_lock_transition(const orc_model* m, const orc_run* r, int t, int M,
                              const int32_t* row_seq, const int32_t* row_pos,
                              const uint8_t* row_real, const int32_t* argmax, const double* conf,
                              const double* kl, const uint8_t* has_kl, int32_t* x,
-                             uint8_t* locked, int32_t* cnt) {
+                             uint8_t* locked, int32_t* cnt, const uint8_t* refresh,
+                             float* drift) {
   lock_transition(*m, *r, t, M, row_seq, row_pos, row_real, argmax, conf, kl, has_kl, x, locked,
-                  cnt, nullptr, nullptr, nullptr);
+                  cnt, nullptr, nullptr, nullptr, true, true, nullptr, nullptr, nullptr, refresh,
+                  drift);
   return 0;
+}
+// Refresh set from the lock state and drift ([B][N] each); refresh rewritten.
+void orc_unit_refresh_select(const orc_run* r, const uint8_t* locked, const float* drift,
+                             uint8_t* refresh) {
+  refresh_select(*r, locked, drift, refresh);
 }
 // One SlowFast commit decision for one sequence on given rows; state
 // [13] = phase, lo, hi, slow_n, hist_n, hist[8] in and out; commits (at most

@@ -3,8 +3,8 @@
 // UndefinedBehaviorSanitizer by tests/test_oracle_sanitizers.py, it calls
 // every exported oracle function on small shapes with fixed pseudo-random
 // inputs: both storage modes, MHA and GQA, both lock policies and KL
-// directions, the semi-autoregressive and SlowFast samplers, commit / lock /
-// counter overrides, a sampled step, and each unit routine.  Any invalid
+// directions, the semi-autoregressive and SlowFast samplers, the drift-aware
+// refresh of locked positions, commit / lock / counter overrides, a sampled step, and each unit routine.  Any invalid
 // access or undefined behaviour aborts with the sanitizer's report; a clean
 // run prints "sanitized run ok".
 #include <cstdint>
@@ -26,7 +26,7 @@ std::vector<float> mat(size_t n, double scale) {
   return v;
 }
 
-int run_model(int nq, int nkv, int bf16, int policy, int sampler, int kl_dir) {
+int run_model(int nq, int nkv, int bf16, int policy, int sampler, int kl_dir, int refresh = 0) {
   orc_model m{2, 32, nq, nkv, 32 / nq, 48, 40, 39, 10000.0, 1e-5, bf16};
   const int L = m.n_layers, d = m.d_model, hd = m.head_dim, dff = m.d_ff, V = m.vocab;
   const int qkv = (nq + 2 * nkv) * hd;
@@ -49,6 +49,8 @@ int run_model(int nq, int nkv, int bf16, int policy, int sampler, int kl_dir) {
   r.sf_tau_conv = 0.0;
   r.sf_tau_high = 0.5;
   r.sf_var = 1.0;
+  r.refresh_budget = refresh;
+  r.refresh_eps = 1e-6;
   auto emb = mat((size_t)V * d, 0.5), fn = mat(d, 1.0), lm = mat((size_t)V * d, 0.2);
   std::vector<std::vector<float>> an(L), wq(L), wo(L), ff(L), wg(L), wu(L), wd(L);
   std::vector<const float*> pan(L), pwq(L), pwo(L), pff(L), pwg(L), pwu(L), pwd(L);
@@ -67,7 +69,8 @@ int run_model(int nq, int nkv, int bf16, int policy, int sampler, int kl_dir) {
   if (!s) return 1;
   const int BN = r.batch * r.seq_len;
   std::vector<int32_t> tok(BN), cnt(BN), sf(r.batch * 13);
-  std::vector<uint8_t> lk(BN), hp(BN), fz(BN);
+  std::vector<uint8_t> lk(BN), hp(BN), fz(BN), rf(BN);
+  std::vector<float> dr(BN);
   for (int t = 0; t < r.steps; ++t) {
     if (orc_step(s) != 0) return 2;
     const int M = orc_m(s);
@@ -98,6 +101,7 @@ int run_model(int nq, int nkv, int bf16, int policy, int sampler, int kl_dir) {
     }
     orc_get_tokens(s, tok.data()); orc_get_locked(s, lk.data()); orc_get_cnt(s, cnt.data());
     orc_get_has_prev(s, hp.data()); orc_get_frozen(s, fz.data()); orc_get_sf(s, sf.data());
+    orc_get_drift(s, dr.data()); orc_get_refresh(s, rf.data());
     std::vector<int32_t> c0(orc_n_commits(s)), c1(c0.size()), c2(c0.size());
     orc_get_commits(s, c0.data(), c1.data(), c2.data());
   }
@@ -153,8 +157,24 @@ int run_units() {
   std::vector<int32_t> xx(r.seq_len, V - 1), cn(r.seq_len, 0);
   if (orc_unit_lock_transition(&m, &r, 0, 3, lseq.data(), lpos.data(), lreal.data(),
                                larg.data(), lconf.data(), lkl.data(), lhk.data(), xx.data(),
-                               locked.data(), cn.data()) != 0)
+                               locked.data(), cn.data(), nullptr, nullptr) != 0)
     return 7;
+  {  // the same transition with a refresh set and drift
+    orc_run rr = r;
+    rr.refresh_budget = 2;
+    rr.refresh_eps = 1e-3;
+    std::vector<uint8_t> rlock(r.seq_len, 0), rsel(r.seq_len, 0);
+    std::vector<float> rdrift(r.seq_len, 0.f);
+    rlock[1] = rlock[5] = rlock[30] = 1;
+    rdrift[5] = 2e-3f;
+    rdrift[30] = INFINITY;
+    orc_unit_refresh_select(&rr, rlock.data(), rdrift.data(), rsel.data());
+    std::vector<int32_t> rcnt(r.seq_len, 0), rx(r.seq_len, V - 1);
+    if (orc_unit_lock_transition(&m, &rr, 1, 3, lseq.data(), lpos.data(), lreal.data(),
+                                 larg.data(), lconf.data(), lkl.data(), lhk.data(), rx.data(),
+                                 rlock.data(), rcnt.data(), rsel.data(), rdrift.data()) != 0)
+      return 8;
+  }
   std::vector<uint64_t> bits = {0x5ull, 0x3Full, ~0ull, 0ull};  // [2 sequences][2 words]
   std::vector<int32_t> cseq(2 * 70), cpos(2 * 70), mb(2);
   (void)orc_unit_compact(bits.data(), 2, 70, cseq.data(), cpos.data(), mb.data());
@@ -183,6 +203,7 @@ int main() {
         rc = run_model(4, 4, bf16, policy, sampler, bf16);
         if (!rc) rc = run_model(4, 2, bf16, policy, sampler, 1 - bf16);
       }
+  for (int bf16 = 0; bf16 < 2 && !rc; ++bf16) rc = run_model(4, 2, bf16, 1, 0, bf16, 3);
   if (rc) {
     std::printf("driver step failed: %d\n", rc);
     return rc;

@@ -81,6 +81,13 @@ LOCK_SETTINGS = {
     "slowfast": dict(policy="test", kl_eps=1e-3, conf_tau=0.9, n_consec=2,
                      lock_prompt_after_first_step=1, sampler="slowfast", sf_k=3, sf_kmax=8,
                      sf_whist=2, sf_tau_conv=0.9, sf_tau_high=0.9, sf_var=1.0),
+    # the scheduled lock test with the drift-aware refresh of locked positions
+    # (Polestar page, Polestar-Cache): each step the 8 locked positions of a
+    # sequence with the largest drift are recomputed, and one whose drift
+    # exceeds 1e-3 (the KL level of the lock test) is unlocked; the budget is
+    # a run choice (the page gives none)
+    "refresh": dict(policy="test", kl_eps=float("inf"), conf_tau=0.0, n_consec=2,
+                    lock_prompt_after_first_step=1, refresh_budget=8, refresh_eps=1e-3),
 }
 
 
