@@ -10,8 +10,10 @@ statistics) + dlm_lock_update (top-k unmasking and the lock test).  The timed
 steps follow a decoding run from its first step (a new run starts every
 128 steps).  `value` is the configured lock setting (KL <= 1e-3, max-prob >=
 0.9, 2 consecutive steps); the scheduled-lock and vanilla (no locking) runs,
-and the configured lock test with the SlowFast sampler in place of the
-semi-autoregressive top-k, are reported alongside.
+the configured lock test with the SlowFast sampler in place of the
+semi-autoregressive top-k, and the scheduled lock test with the drift-aware
+refresh of locked positions (8 recomputed per step, unlocked above a drift of
+1e-3) are reported alongside.
 
 Per-kernel times come from HIP events recorded on the engine's stream in a
 second pass over the same steps; the roofline entry is for the kernel class
@@ -475,7 +477,7 @@ def main():
     K, Wm = args.steps, args.warmup
     results = {}
     settings = ["natural"] + ([] if args.no_extra_settings
-                              else ["scheduled", "vanilla", "slowfast"])
+                              else ["scheduled", "vanilla", "slowfast", "refresh"])
     for s in settings:
         if Wm > 0:
             run_steps(factory(s), Wm)
@@ -488,7 +490,7 @@ def main():
     # scheduled setting's locking shows only over a whole run
     whole = {}
     if not args.no_whole_runs:
-        for s in ("natural", "scheduled", "vanilla"):
+        for s in ("natural", "scheduled", "refresh", "vanilla"):
             run_steps(factory(s), run.steps)
             fls = []
             dt, toks, ms, _ = run_steps(factory(s), run.steps, flops_out=fls)
@@ -499,7 +501,7 @@ def main():
             log(f"[whole run/{s}] {run.steps} steps in {dt:.3f} s -> {run.steps / dt:.1f} steps/s, "
                 f"mean M {sum(ms) / len(ms):.1f}")
         v = whole["vanilla"]
-        for s in ("natural", "scheduled"):
+        for s in ("natural", "scheduled", "refresh"):
             whole[s]["speedup_vs_vanilla"] = round(v["seconds"] / whole[s]["seconds"], 3)
             whole[s]["flop_saving_vs_vanilla"] = round(1.0 - whole[s]["tflop"] / v["tflop"], 4)
 

@@ -108,13 +108,29 @@ typedef struct {
  * masked positions beyond the span leave the active set (frozen: their K/V
  * and last prediction stand), and once the span is decoded they return
  * without a previous posterior (no KL on their first step back) and a new
- * cycle starts.  The other sf_ fields are ignored for the semi-AR sampler. */
+ * cycle starts.  The other sf_ fields are ignored for the semi-AR sampler.
+ *
+ * refresh_budget > 0 turns on the drift-aware refresh of locked positions
+ * (Polestar page, "Polestar: Drift-Aware Cache Calibration and Token
+ * Commitment ...", section "Polestar: The Smart Painter", Polestar-Cache:
+ * recompute only the cached positions whose distribution drifts most, the
+ * drift measured by a KL divergence).  A position's drift is the KL (kl_dir's
+ * direction) between its two most recent posteriors, +inf while undefined.
+ * At the start of every step, the refresh_budget locked positions of each
+ * sequence with the largest drift (ties: smaller position) rejoin the active
+ * set: their K/V are recomputed and their drift measured against the
+ * posterior they had when last computed.  At the lock update a recomputed
+ * position stays locked if that drift is at most refresh_eps and is unlocked
+ * (counter cleared) otherwise; the lock test does not apply to it.  Requires
+ * the semi-AR sampler and refresh_budget <= seq_len; 0 turns it off. */
 typedef struct {
   int32_t batch, seq_len, prompt_len, steps, block_len;
   float kl_eps, conf_tau;
   int32_t n_consec, kl_dir, lock_prompt_after_first_step, lock_policy;
   int32_t sampler, sf_k, sf_kmax, sf_whist;
   float sf_tau_conv, sf_tau_high, sf_var;
+  int32_t refresh_budget;
+  float refresh_eps;
 } dlm_run_desc;
 
 /* Replay override for dlm_lock_update (host pointers).  n_commit >= 0 replaces
@@ -122,7 +138,8 @@ typedef struct {
  * sampler the cycle state and frozen set are then left as they were); lock_bits non-null
  * replaces the lock test: bits |= lock_bits ([batch][ceil(seq_len/64)]) and
  * the counters are set from counters ([batch][seq_len]) when non-null, else
- * kept. */
+ * kept.  With the refresh on, lock_bits also decides the positions the step
+ * recomputed while locked: such a position stays locked iff its bit is set. */
 typedef struct {
   const int32_t* commit_seq;
   const int32_t* commit_pos;
@@ -187,7 +204,10 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out);
  * DLM_SAMPLER_SLOWFAST).  Lock: the KL test with the confidence gate and the
  * monotone bitmask update (SureLock page, §2 Methodology: locking condition
  * KL(p_t || p_{t-1}) <= eps with an optional confidence gate; permanent
- * deactivation).  ov (nullable, host memory) replays given decisions in
+ * deactivation); with the refresh on, a recomputed locked position is kept
+ * or unlocked by its drift against refresh_eps (Polestar page, "The Smart
+ * Painter", Polestar-Cache) and every row's drift is recorded.  ov
+ * (nullable, host memory) replays given decisions in
  * place of the rule (see dlm_override).  If the step latched a non-finite
  * posterior, neither commits nor locks happen (the error is returned by the
  * next dlm_step).  Asynchronous except for the copy of override arrays.
@@ -222,7 +242,11 @@ enum {
   DLM_GET_SF_STATE = 15, /* int32  [batch][16] SlowFast cycle: phase (0 exploratory, 1
                             accelerated), span lo, span hi (exclusive), exploratory steps,
                             recorded end points n, the last n end points (up to 8), 3 unused */
-  DLM_GET_HAS_PREV = 16  /* int32  [batch][seq_len] a previous-step posterior is stored */
+  DLM_GET_HAS_PREV = 16, /* int32  [batch][seq_len] a previous-step posterior is stored */
+  DLM_GET_DRIFT = 17,    /* float  [batch][seq_len] KL between the two latest posteriors
+                            (+inf while undefined; kept only with the refresh on) */
+  DLM_GET_REFRESH = 18   /* uint64 [batch][ceil(seq_len/64)] locked positions this step
+                            recomputed (refresh on) */
 };
 int dlm_get(dlm_handle* h, int32_t what, const void** dev_ptr, int64_t* n);
 

@@ -20,7 +20,7 @@ DLM_SAMPLER_SEMI_AR, DLM_SAMPLER_SLOWFAST = 0, 1
 (DLM_GET_TOKENS, DLM_GET_LOCK_BITS, DLM_GET_COUNTERS, DLM_GET_ROW_SEQ, DLM_GET_ROW_POS,
  DLM_GET_ARGMAX, DLM_GET_CONF, DLM_GET_KL, DLM_GET_HAS_KL, DLM_GET_LSE, DLM_GET_LOGITS,
  DLM_GET_ROW_REAL, DLM_GET_KCACHE, DLM_GET_VCACHE, DLM_GET_FROZEN, DLM_GET_SF_STATE,
- DLM_GET_HAS_PREV) = range(17)
+ DLM_GET_HAS_PREV, DLM_GET_DRIFT, DLM_GET_REFRESH) = range(19)
 SF_STATE_INTS = 16
 KCLASSES = ["compact", "embed_norm", "rmsnorm", "gemm_qkv", "rope_kv", "attention", "gemm_o",
             "gemm_gate_up", "gemm_down", "gemm_lm_head", "vocab_stats", "commit_lock"]
@@ -67,7 +67,8 @@ class dlm_run_desc(ctypes.Structure):
                 ("block_len", i32), ("kl_eps", f32), ("conf_tau", f32), ("n_consec", i32),
                 ("kl_dir", i32), ("lock_prompt_after_first_step", i32), ("lock_policy", i32),
                 ("sampler", i32), ("sf_k", i32), ("sf_kmax", i32), ("sf_whist", i32),
-                ("sf_tau_conv", f32), ("sf_tau_high", f32), ("sf_var", f32)]
+                ("sf_tau_conv", f32), ("sf_tau_high", f32), ("sf_var", f32),
+                ("refresh_budget", i32), ("refresh_eps", f32)]
 
 
 class dlm_override(ctypes.Structure):

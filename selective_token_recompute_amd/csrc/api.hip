@@ -34,7 +34,7 @@ inline size_t al(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Offsets of every array inside state_mem.
 struct Layout {
   size_t tokens, bits, counters, has_prev, row_seq, row_pos, m_b, row_start, ctl, row_real;
-  size_t frozen, sf_state;
+  size_t frozen, sf_state, drift, last_step, refresh, rlist;
   size_t argmax, conf, kl, has_kl, lse_row, lse[2], z[2], kc, vc, rope, h, a, qkv, q, o, u;
   size_t ws, ws_bytes, ov_cseq, ov_cpos, ov_ctok, ov_bits, ov_cnt, total;
 };
@@ -70,6 +70,11 @@ bool valid_run(const dlm_run_desc* r) {
   if (r->sampler == DLM_SAMPLER_SLOWFAST &&
       (r->seq_len > 4096 || r->sf_k < 1 || r->sf_kmax < 1 || r->sf_whist < 1 || r->sf_whist > 8 ||
        std::isnan(r->sf_tau_conv) || std::isnan(r->sf_tau_high) || std::isnan(r->sf_var)))
+    return false;
+  // drift-aware refresh: semi-AR sampler, one sequence's keys in 32 KB of LDS
+  if (r->refresh_budget < 0 || r->refresh_budget > r->seq_len || std::isnan(r->refresh_eps))
+    return false;
+  if (r->refresh_budget > 0 && (r->sampler != DLM_SAMPLER_SEMI_AR || r->seq_len > 4096))
     return false;
   return true;
 }
@@ -109,6 +114,10 @@ Layout make_layout(const dlm_model_desc& m, const dlm_run_desc& r) {
   L.bits = take(B * W * 8);
   L.frozen = take(B * W * 8);
   L.sf_state = take(B * kSfStateInts * 4);
+  L.drift = take(BN * 4);
+  L.last_step = take(BN * 4);
+  L.refresh = take(B * W * 8);
+  L.rlist = take(B * std::max<size_t>(1, (size_t)r.refresh_budget) * 4);
   L.counters = take(BN * 4);
   L.has_prev = take(BN * 4);
   L.row_seq = take(BN * 4);
@@ -362,6 +371,13 @@ int dlm_step_init(const dlm_model_desc* model, const dlm_weights* w, const dlm_r
                                    h->at<int32_t>(lay.counters), h->at<int32_t>(lay.has_prev),
                                    h->at<int32_t>(lay.ctl), h->at<uint64_t>(lay.frozen),
                                    h->at<int32_t>(lay.sf_state), h->stream);
+  // drift +inf (undefined), last computed at no step (-1), nothing refreshed
+  if (e == hipSuccess)
+    e = launch_fill_u32(h->base + lay.drift, (size_t)B * N * 4, 0x7f800000u, h->stream);
+  if (e == hipSuccess)
+    e = launch_fill_u32(h->base + lay.last_step, (size_t)B * N * 4, 0xffffffffu, h->stream);
+  if (e == hipSuccess)
+    e = launch_fill_u32(h->base + lay.refresh, (size_t)B * ((N + 63) / 64) * 8, 0u, h->stream);
   if (e == hipSuccess && model->rope_base > 0.f)
     e = launch_rope_table(N, model->head_dim, model->rope_base, h->at<float>(lay.rope), h->stream);
   if (e != hipSuccess) {
@@ -388,10 +404,29 @@ int dlm_step(dlm_handle* h, int32_t* m_tot_out) {
   int32_t* row_pos = h->at<int32_t>(y.row_pos);
   int32_t* row_start = h->at<int32_t>(y.row_start);
   int32_t* ctl = h->at<int32_t>(y.ctl);
+  const bool refresh = r.refresh_budget > 0;
+  if (refresh) {
+    // drift-aware refresh (Polestar page, "The Smart Painter", Polestar-Cache):
+    // choose the locked positions to recompute, and put each one's last
+    // posterior where this step reads the previous one
+    TRY(timed(h, DLM_K_COMPACT, 0.0, 0.0, [&] {
+      return launch_refresh_select(B, N, r.refresh_budget, h->at<uint64_t>(y.bits),
+                                   h->at<float>(y.drift), h->at<uint64_t>(y.refresh),
+                                   h->at<int32_t>(y.rlist), s);
+    }));
+    TRY(timed(h, DLM_K_COMPACT, 0.0, 0.0, [&] {
+      return launch_refresh_copy(B, N, V, r.refresh_budget, h->t, h->at<int32_t>(y.rlist),
+                                 h->at<int32_t>(y.last_step), h->at<float>(y.z[0]),
+                                 h->at<float>(y.z[1]), h->at<float>(y.lse[0]),
+                                 h->at<float>(y.lse[1]), s);
+    }));
+  }
   TRY(timed(h, DLM_K_COMPACT, B * ((N + 63) / 64) * 8.0, 0.0, [&] {
     return launch_compact(h->at<uint64_t>(y.bits),
                           r.sampler == DLM_SAMPLER_SLOWFAST ? h->at<uint64_t>(y.frozen) : nullptr,
-                          B, N, row_seq, row_pos, h->at<int32_t>(y.m_b), row_start, ctl, s);
+                          B, N, row_seq, row_pos, h->at<int32_t>(y.m_b), row_start, ctl, s,
+                          refresh ? h->at<uint64_t>(y.refresh) : nullptr,
+                          refresh ? h->at<int32_t>(y.last_step) : nullptr, h->t);
   }));
   int32_t hctl[2] = {0, 0};
   TRY(hipMemcpyAsync(hctl, ctl, sizeof(hctl), hipMemcpyDeviceToHost, s));
@@ -577,7 +612,11 @@ int dlm_lock_update(dlm_handle* h, const dlm_override* ov) {
   la.has_prev = h->at<int32_t>(y.has_prev);
   la.sf_state = h->at<int32_t>(y.sf_state);
   la.err = h->at<int32_t>(y.ctl) + 1;
-  if (la.do_commit || la.do_lock)
+  const bool refresh = r.refresh_budget > 0;
+  la.refresh = refresh ? h->at<uint64_t>(y.refresh) : nullptr;
+  la.refresh_eps = r.refresh_eps;
+  la.drift = refresh ? h->at<float>(y.drift) : nullptr;
+  if (la.do_commit || la.do_lock || la.drift)
     TRY(timed(h, DLM_K_COMMIT_LOCK, 0.0, 0.0, [&] { return launch_commit_lock(la, h->stream); }));
   if (ov && (ov_commit || ov_lock)) {
     const int nc = ov_commit ? ov->n_commit : 0;
@@ -601,7 +640,8 @@ int dlm_lock_update(dlm_handle* h, const dlm_override* ov) {
                               ov_lock ? h->at<uint64_t>(y.ov_bits) : nullptr,
                               (ov_lock && ov->counters) ? h->at<int32_t>(y.ov_cnt) : nullptr,
                               h->at<int32_t>(y.tokens), h->at<uint64_t>(y.bits),
-                              h->at<int32_t>(y.counters), h->stream));
+                              h->at<int32_t>(y.counters), h->stream,
+                              refresh ? h->at<uint64_t>(y.refresh) : nullptr));
     // the host arrays may be released as soon as this call returns
     TRY(hipStreamSynchronize(h->stream));
   }
@@ -637,6 +677,8 @@ int dlm_get(dlm_handle* h, int32_t what, const void** dev_ptr, int64_t* n) {
     case DLM_GET_FROZEN: off = y.frozen; cnt = B * ((N + 63) / 64); break;
     case DLM_GET_SF_STATE: off = y.sf_state; cnt = B * kSfStateInts; break;
     case DLM_GET_HAS_PREV: off = y.has_prev; cnt = BN; break;
+    case DLM_GET_DRIFT: off = y.drift; cnt = BN; break;
+    case DLM_GET_REFRESH: off = y.refresh; cnt = B * ((N + 63) / 64); break;
     default: return DLM_E_INVALID;
   }
   *dev_ptr = h->base + off;
@@ -675,13 +717,14 @@ namespace {
 // Checkpoint image: a 256-byte header, then three byte ranges of the state
 // copied as they lie: the per-position and per-row arrays (tokens through
 // the two log-normaliser buffers, contiguous in the layout), the logits
-// buffer the next step reads as the previous posterior, and the K and V
-// caches (contiguous).
+// buffer the next step reads as the previous posterior (with the refresh on,
+// then also the other one: a locked position's last posterior may lie in
+// either), and the K and V caches (contiguous).
 constexpr char kCkptMagic[8] = {'D', 'L', 'M', 'C', 'K', 'P', 'T', '1'};
 constexpr uint32_t kCkptVersion = 1;
 constexpr size_t kCkptHeaderBytes = 256;
 static_assert(sizeof(dlm_model_desc) == 11 * 4, "model descriptor without padding");
-static_assert(sizeof(dlm_run_desc) == 18 * 4, "run descriptor without padding");
+static_assert(sizeof(dlm_run_desc) == 20 * 4, "run descriptor without padding");
 
 struct CkptHeader {
   char magic[8];
@@ -703,7 +746,7 @@ CkptParts ckpt_parts(const dlm_handle* h) {
   CkptParts c;
   c.small_off = y.tokens;
   c.small_bytes = y.z[0] - y.tokens;
-  c.z_bytes = (size_t)h->r.batch * h->r.seq_len * h->m.vocab * 4;
+  c.z_bytes = (size_t)h->r.batch * h->r.seq_len * h->m.vocab * 4 * (h->r.refresh_budget > 0 ? 2 : 1);
   c.kv_off = y.kc;
   c.kv_bytes = y.rope - y.kc;
   c.total = kCkptHeaderBytes + c.small_bytes + c.z_bytes + c.kv_bytes;
@@ -712,6 +755,8 @@ CkptParts ckpt_parts(const dlm_handle* h) {
 
 // logits buffer that the handle's next step reads as the previous posterior
 size_t ckpt_prev_z(const dlm_handle* h) { return h->lay.z[(h->t & 1) ^ 1]; }
+// the other logits buffer
+size_t ckpt_cur_z(const dlm_handle* h) { return h->lay.z[h->t & 1]; }
 }  // namespace
 
 extern "C" {
@@ -744,7 +789,12 @@ int dlm_checkpoint_save(dlm_handle* h, void* dst, size_t dst_bytes) {
   d += kCkptHeaderBytes;
   TRY(hipMemcpyAsync(d, h->base + c.small_off, c.small_bytes, hipMemcpyDefault, h->stream));
   d += c.small_bytes;
-  TRY(hipMemcpyAsync(d, h->base + ckpt_prev_z(h), c.z_bytes, hipMemcpyDefault, h->stream));
+  {
+    const size_t zb = (size_t)h->r.batch * h->r.seq_len * h->m.vocab * 4;
+    TRY(hipMemcpyAsync(d, h->base + ckpt_prev_z(h), zb, hipMemcpyDefault, h->stream));
+    if (c.z_bytes > zb)
+      TRY(hipMemcpyAsync(d + zb, h->base + ckpt_cur_z(h), zb, hipMemcpyDefault, h->stream));
+  }
   d += c.z_bytes;
   TRY(hipMemcpyAsync(d, h->base + c.kv_off, c.kv_bytes, hipMemcpyDefault, h->stream));
   TRY(hipStreamSynchronize(h->stream));  // hd_bytes lives on this stack frame
@@ -772,7 +822,12 @@ int dlm_checkpoint_load(dlm_handle* h, const void* src, size_t src_bytes) {
   const unsigned char* s = static_cast<const unsigned char*>(src) + kCkptHeaderBytes;
   TRY(hipMemcpyAsync(h->base + c.small_off, s, c.small_bytes, hipMemcpyDefault, h->stream));
   s += c.small_bytes;
-  TRY(hipMemcpyAsync(h->base + ckpt_prev_z(h), s, c.z_bytes, hipMemcpyDefault, h->stream));
+  {
+    const size_t zb = (size_t)h->r.batch * h->r.seq_len * h->m.vocab * 4;
+    TRY(hipMemcpyAsync(h->base + ckpt_prev_z(h), s, zb, hipMemcpyDefault, h->stream));
+    if (c.z_bytes > zb)
+      TRY(hipMemcpyAsync(h->base + ckpt_cur_z(h), s + zb, zb, hipMemcpyDefault, h->stream));
+  }
   s += c.z_bytes;
   TRY(hipMemcpyAsync(h->base + c.kv_off, s, c.kv_bytes, hipMemcpyDefault, h->stream));
   TRY(hipStreamSynchronize(h->stream));

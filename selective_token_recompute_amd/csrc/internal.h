@@ -16,10 +16,26 @@ enum Epi {
 };
 
 // ---- compaction -------------------------------------------------------------
-// frozen (nullable): positions also out of the active set
+// frozen (nullable): positions also out of the active set; refresh
+// (nullable): locked positions that are active this step; last_step
+// (nullable): [B][N] set to t for every active position
 hipError_t launch_compact(const uint64_t* bits, const uint64_t* frozen, int B, int N,
                           int32_t* row_seq, int32_t* row_pos, int32_t* m_b, int32_t* row_start,
-                          int32_t* ctl, hipStream_t s);
+                          int32_t* ctl, hipStream_t s, const uint64_t* refresh = nullptr,
+                          int32_t* last_step = nullptr, int t = 0);
+// Drift-aware refresh (Polestar page, "The Smart Painter", Polestar-Cache):
+// per sequence, the `budget` locked positions with the largest drift (ties:
+// smaller position) into refresh [B][ceil(N/64)] (rewritten) and rlist
+// [B][budget] (position by rank, -1 past the candidates).  N <= 4096.
+hipError_t launch_refresh_select(int B, int N, int budget, const uint64_t* bits,
+                                 const float* drift, uint64_t* refresh, int32_t* rlist,
+                                 hipStream_t s);
+// Puts each listed position's last posterior (logits row and log-normaliser,
+// in the buffer of the step that last computed it, last_step & 1) into the
+// buffer that step t reads as the previous one ((t - 1) & 1).
+hipError_t launch_refresh_copy(int B, int N, int V, int budget, int t, const int32_t* rlist,
+                               const int32_t* last_step, float* z0, float* z1, float* lse0,
+                               float* lse1, hipStream_t s);
 
 // ---- norms / embedding / rotary ----------------------------------------------
 hipError_t launch_embed_rmsnorm(int dtype, int M, int d, int N, float eps, int mask_id,
@@ -164,13 +180,21 @@ struct LockArgs {
   // nullable: the device word the statistics latch on a non-finite
   // log-normaliser; while it is set the kernel commits and locks nothing
   const int32_t* err;
+  // drift-aware refresh (nullable when off): the locked positions this step
+  // recomputed [B][ceil(N/64)], the drift above which one is unlocked, and
+  // every position's drift [B][N] (written for each row of the step)
+  const uint64_t* refresh;
+  float refresh_eps;
+  float* drift;
 };
 constexpr int kSfStateInts = 16;  // phase, lo, hi, slow_n, hist_n, hist[8], 3 unused
 hipError_t launch_commit_lock(const LockArgs& a, hipStream_t s);
+// refresh (nullable): positions whose lock bit the override sets outright
+// (bits = bits & ~refresh | bits_or) rather than ORs
 hipError_t launch_apply_override(int B, int N, int n_commit, const int32_t* cseq,
                                  const int32_t* cpos, const int32_t* ctok, const uint64_t* bits_or,
                                  const int32_t* counters, int32_t* tokens, uint64_t* bits,
-                                 int32_t* cnt, hipStream_t s);
+                                 int32_t* cnt, hipStream_t s, const uint64_t* refresh = nullptr);
 // Fills bytes / 4 words at p with the pattern v.
 hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t v, hipStream_t s);
 hipError_t launch_init_state(int B, int N, int P, int mask_id, const int32_t* prompts,

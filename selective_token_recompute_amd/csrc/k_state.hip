@@ -12,6 +12,11 @@
 // top-k while the convergence end point settles, then every high-confidence
 // position of the stable span at once, positions beyond the span kept out of
 // the active set until the span is decoded).
+// Polestar page ("Polestar: Drift-Aware Cache Calibration and Token
+// Commitment ..."), section "Polestar: The Smart Painter", Polestar-Cache:
+// optionally, the locked positions whose distribution drifted most (KL
+// between a position's two latest posteriors) are recomputed, and unlocked
+// when the drift measured then exceeds a threshold.
 #include "common.h"
 #include "internal.h"
 
@@ -76,13 +81,23 @@ hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t v, hipStream_t s) {
 // wave's base is the prefix over the wave counts of this chunk.
 constexpr int kCompactThreads = 1024;
 
-// A position is active when its lock bit and (if given) its frozen bit are
-// both clear.
+// A position is active when its lock bit (unless the refresh recomputes it)
+// and its frozen bit (if given) are both clear; with last_step given, every
+// active position records the step t.
+__device__ __forceinline__ uint64_t inactive_word(const uint64_t* bits, const uint64_t* frozen,
+                                                  const uint64_t* refresh, size_t w) {
+  uint64_t word = bits[w];
+  if (refresh) word &= ~refresh[w];
+  if (frozen) word |= frozen[w];
+  return word;
+}
+
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
     const uint64_t* __restrict__ bits, const uint64_t* __restrict__ frozen, int B, int N,
     int32_t* __restrict__ row_seq,
     int32_t* __restrict__ row_pos, int32_t* __restrict__ m_b, int32_t* __restrict__ row_start,
-    int32_t* __restrict__ ctl) {
+    int32_t* __restrict__ ctl, const uint64_t* __restrict__ refresh,
+    int32_t* __restrict__ last_step, int t) {
   __shared__ int wave_cnt[kCompactThreads / 64];
   __shared__ int base_s;
   __shared__ int mb_s[1024];
@@ -98,8 +113,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
     if (f < total) {
       b = f / N;
       i = f - b * N;
-      uint64_t word = bits[(size_t)b * W + (i >> 6)];
-      if (frozen) word |= frozen[(size_t)b * W + (i >> 6)];
+      const uint64_t word = inactive_word(bits, frozen, refresh, (size_t)b * W + (i >> 6));
       act = !((word >> (i & 63)) & 1ull);
     }
     const uint64_t ballot = __ballot(act);
@@ -112,6 +126,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
     if (act) {
       row_seq[off + below] = b;
       row_pos[off + below] = i;
+      if (last_step) last_step[f] = t;
     }
     __syncthreads();
     if (tid == 0) {
@@ -125,7 +140,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
   for (int b = tid; b < B; b += kCompactThreads) {
     int cnt = 0;
     for (int wd = 0; wd < W; ++wd) {
-      uint64_t v = ~(bits[(size_t)b * W + wd] | (frozen ? frozen[(size_t)b * W + wd] : 0ull));
+      uint64_t v = ~inactive_word(bits, frozen, refresh, (size_t)b * W + wd);
       const int valid = N - wd * 64;
       if (valid < 64) v &= (1ull << valid) - 1ull;
       cnt += __popcll(v);
@@ -147,9 +162,10 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
 
 hipError_t launch_compact(const uint64_t* bits, const uint64_t* frozen, int B, int N,
                           int32_t* row_seq, int32_t* row_pos, int32_t* m_b, int32_t* row_start,
-                          int32_t* ctl, hipStream_t s) {
+                          int32_t* ctl, hipStream_t s, const uint64_t* refresh,
+                          int32_t* last_step, int t) {
   compact_kernel<<<1, kCompactThreads, 0, s>>>(bits, frozen, B, N, row_seq, row_pos, m_b,
-                                               row_start, ctl);
+                                               row_start, ctl, refresh, last_step, t);
   return hipGetLastError();
 }
 
@@ -247,6 +263,23 @@ __device__ void or_position_bits(uint64_t* bits, bool set, int pos) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o);
     if (lane == leader) atomicOr((unsigned long long*)&bits[w0], v);
+    pending = pending && !mine;
+  }
+}
+
+// bits[pos / 64] &= ~(1 << (pos % 64)) for the lanes with `clear`, one
+// atomic AND per distinct word per wave.  Every lane of the wave calls it.
+__device__ void clear_position_bits(uint64_t* bits, bool clear, int pos) {
+  const int lane = threadIdx.x & 63;
+  bool pending = clear;
+  for (uint64_t pend = __ballot(pending); pend; pend = __ballot(pending)) {
+    const int leader = __ffsll((unsigned long long)pend) - 1;
+    const int w0 = __shfl(pos >> 6, leader);
+    const bool mine = pending && (pos >> 6) == w0;
+    unsigned long long v = mine ? (1ull << (pos & 63)) : 0ull;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o);
+    if (lane == leader) atomicAnd((unsigned long long*)&bits[w0], ~v);
     pending = pending && !mine;
   }
 }
@@ -441,22 +474,36 @@ __global__ __launch_bounds__(kLockThreads) void commit_lock_kernel(LockArgs a) {
       if (rank_upto(c, C, ckey, a.k, [](int) { return true; }) < a.k)
         tok[cpos[c]] = a.argmax[crow[c]];
   }
+  // every recomputed position's drift: its KL between this posterior and the
+  // one before (+inf while undefined), whatever decides the lock state
+  if (a.drift)
+    for (int r = r0 + tid; r < r1; r += kLockThreads)
+      a.drift[(size_t)b * N + a.row_pos[r]] = a.has_kl[r] ? a.kl[r] : INFINITY;
   if (a.do_lock && a.policy == 1) {
     uint64_t* bw = a.bits + (size_t)b * W;
+    const uint64_t* rw = a.refresh ? a.refresh + (size_t)b * W : nullptr;
     for (int c0 = r0; c0 < r1; c0 += kLockThreads) {
       const int r = c0 + tid;
       int pos = 0;
-      bool lock = false;
+      bool lock = false, unlock = false;
       if (r < r1) {
         pos = a.row_pos[r];
-        const bool pass = a.row_real[r] && a.has_kl[r] && (a.kl[r] <= a.kl_eps) &&
-                          (a.conf[r] >= a.conf_tau);
         int32_t* cnt = a.counters + (size_t)b * N + pos;
-        const int c = pass ? *cnt + 1 : 0;
-        *cnt = c;
-        lock = c >= a.n_consec;
+        if (rw && ((rw[pos >> 6] >> (pos & 63)) & 1ull)) {
+          // recomputed while locked: kept while the drift is defined and at
+          // most refresh_eps, unlocked (counter cleared) otherwise
+          unlock = !(a.has_kl[r] && a.kl[r] <= a.refresh_eps);
+          if (unlock) *cnt = 0;
+        } else {
+          const bool pass = a.row_real[r] && a.has_kl[r] && (a.kl[r] <= a.kl_eps) &&
+                            (a.conf[r] >= a.conf_tau);
+          const int c = pass ? *cnt + 1 : 0;
+          *cnt = c;
+          lock = c >= a.n_consec;
+        }
       }
       or_position_bits(bw, lock, pos);
+      if (rw) clear_position_bits(bw, unlock, pos);
     }
     if (a.lock_prompt) {
       for (int wd = tid; wd * 64 < a.P; wd += kLockThreads) {
@@ -483,7 +530,8 @@ hipError_t launch_commit_lock(const LockArgs& a, hipStream_t s) {
 __global__ void apply_override_kernel(int B, int N, int n_commit, const int32_t* cseq,
                                       const int32_t* cpos, const int32_t* ctok,
                                       const uint64_t* bits_or, const int32_t* counters,
-                                      int32_t* tokens, uint64_t* bits, int32_t* cnt) {
+                                      int32_t* tokens, uint64_t* bits, int32_t* cnt,
+                                      const uint64_t* refresh) {
   const int W = (N + 63) >> 6;
   const size_t bn = (size_t)B * N;
   const size_t nc = n_commit > 0 ? (size_t)n_commit : 0;
@@ -491,7 +539,8 @@ __global__ void apply_override_kernel(int B, int N, int n_commit, const int32_t*
   for (size_t f = blockIdx.x * (size_t)blockDim.x + threadIdx.x; f < total;
        f += (size_t)gridDim.x * blockDim.x) {
     if (f < nc) tokens[(size_t)cseq[f] * N + cpos[f]] = ctok[f];
-    if (bits_or && f < (size_t)B * W) bits[f] |= bits_or[f];
+    if (bits_or && f < (size_t)B * W)
+      bits[f] = (refresh ? bits[f] & ~refresh[f] : bits[f]) | bits_or[f];
     if (counters && f < (size_t)B * N) cnt[f] = counters[f];
   }
 }
@@ -499,11 +548,111 @@ __global__ void apply_override_kernel(int B, int N, int n_commit, const int32_t*
 hipError_t launch_apply_override(int B, int N, int n_commit, const int32_t* cseq,
                                  const int32_t* cpos, const int32_t* ctok, const uint64_t* bits_or,
                                  const int32_t* counters, int32_t* tokens, uint64_t* bits,
-                                 int32_t* cnt, hipStream_t s) {
+                                 int32_t* cnt, hipStream_t s, const uint64_t* refresh) {
   const size_t total = std::max<size_t>((size_t)B * N, (size_t)std::max(n_commit, 0));
   const int grid = (int)std::min<size_t>((total + 255) / 256, 4096);
   apply_override_kernel<<<grid, 256, 0, s>>>(B, N, n_commit, cseq, cpos, ctok, bits_or, counters,
-                                             tokens, bits, cnt);
+                                             tokens, bits, cnt, refresh);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Refresh selection, one workgroup per sequence: the locked positions are
+// gathered into LDS in position order by a wave ballot, each with the key of
+// rank_key (drift in place of confidence: larger drift first, then smaller
+// position); a candidate whose rank (keys above it, counted up to the budget)
+// is below the budget is selected, sets its refresh bit and takes list slot
+// `rank` (ranks are distinct: the keys are).
+constexpr int kRefreshMaxN = 4096;  // keys of one sequence fit 32 KB of LDS
+
+__global__ __launch_bounds__(kLockThreads) void refresh_select_kernel(
+    int N, int budget, const uint64_t* __restrict__ bits, const float* __restrict__ drift,
+    uint64_t* __restrict__ refresh, int32_t* __restrict__ rlist) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint64_t* ckey = reinterpret_cast<uint64_t*>(smem);
+  __shared__ int wcnt[kLockWaves];
+  __shared__ int s_base;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int W = (N + 63) >> 6;
+  const uint64_t* bw = bits + (size_t)b * W;
+  uint64_t* rw = refresh + (size_t)b * W;
+  const float* dr = drift + (size_t)b * N;
+  for (int w = tid; w < W; w += kLockThreads) rw[w] = 0ull;
+  for (int j = tid; j < budget; j += kLockThreads) rlist[(size_t)b * budget + j] = -1;
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  for (int p0 = 0; p0 < N; p0 += kLockThreads) {
+    const int p = p0 + tid;
+    const bool t = p < N && ((bw[p >> 6] >> (p & 63)) & 1ull);
+    const uint64_t bal = __ballot(t);
+    if (lane == 0) wcnt[wv] = __popcll(bal);
+    __syncthreads();
+    int off = s_base;
+    for (int w = 0; w < wv; ++w) off += wcnt[w];
+    if (t) ckey[off + __popcll(bal & ((1ull << lane) - 1ull))] = rank_key(dr[p], p);
+    __syncthreads();
+    if (tid == 0) {
+      int n = s_base;
+      for (int w = 0; w < kLockWaves; ++w) n += wcnt[w];
+      s_base = n;
+    }
+    __syncthreads();
+  }
+  const int C = s_base;
+  if (tid < ((C + 15) & ~15) - C) ckey[C + tid] = 0ull;  // padding ranks behind all
+  __syncthreads();
+  for (int c0 = 0; c0 < C; c0 += kLockThreads) {
+    const int c = c0 + tid;
+    int pos = 0, rank = budget;
+    if (c < C) {
+      pos = key_pos(ckey[c]);
+      rank = rank_upto(c, C, ckey, budget, [](int) { return true; });
+      if (rank < budget) rlist[(size_t)b * budget + rank] = pos;
+    }
+    or_position_bits(rw, rank < budget, pos);
+  }
+}
+
+hipError_t launch_refresh_select(int B, int N, int budget, const uint64_t* bits,
+                                 const float* drift, uint64_t* refresh, int32_t* rlist,
+                                 hipStream_t s) {
+  if (N > kRefreshMaxN || budget < 1) return hipErrorInvalidValue;
+  const size_t lds = (size_t)((N + 15) & ~15) * sizeof(uint64_t);
+  refresh_select_kernel<<<B, kLockThreads, lds, s>>>(N, budget, bits, drift, refresh, rlist);
+  return hipGetLastError();
+}
+
+// Copy of a refreshed position's last posterior into the previous-step
+// buffer: grid (B * budget list entries, vocabulary chunks of 4096).
+constexpr int kCopyChunk = 4096;
+
+__global__ __launch_bounds__(256) void refresh_copy_kernel(int N, int V, int budget, int t,
+                                                           const int32_t* __restrict__ rlist,
+                                                           const int32_t* __restrict__ last_step,
+                                                           float* z0, float* z1, float* lse0,
+                                                           float* lse1) {
+  const int e = blockIdx.x, b = e / budget;
+  const int pos = rlist[e];
+  if (pos < 0) return;
+  const size_t slot = (size_t)b * N + pos;
+  const int ls = last_step[slot];
+  const int src = ls & 1, dst = (t - 1) & 1;
+  if (ls < 0 || src == dst) return;  // already where step t reads it
+  const float* zs = (src ? z1 : z0) + slot * V;
+  float* zd = (dst ? z1 : z0) + slot * V;
+  const int c0 = blockIdx.y * kCopyChunk;
+  const int c1 = min(V, c0 + kCopyChunk);
+  for (int c = c0 + threadIdx.x; c < c1; c += 256) zd[c] = zs[c];
+  if (blockIdx.y == 0 && threadIdx.x == 0) (dst ? lse1 : lse0)[slot] = (src ? lse1 : lse0)[slot];
+}
+
+hipError_t launch_refresh_copy(int B, int N, int V, int budget, int t, const int32_t* rlist,
+                               const int32_t* last_step, float* z0, float* z1, float* lse0,
+                               float* lse1, hipStream_t s) {
+  if (budget < 1 || t < 1) return hipSuccess;
+  const dim3 grid(B * budget, (V + kCopyChunk - 1) / kCopyChunk);
+  refresh_copy_kernel<<<grid, 256, 0, s>>>(N, V, budget, t, rlist, last_step, z0, z1, lse0,
+                                           lse1);
   return hipGetLastError();
 }
 

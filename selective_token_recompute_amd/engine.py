@@ -47,7 +47,9 @@ def run_desc(run, lock: Dict) -> L.dlm_run_desc:
                           float(lock["kl_eps"]), float(lock["conf_tau"]), int(lock["n_consec"]),
                           int(lock.get("kl_dir", 0)), int(lock["lock_prompt_after_first_step"]),
                           pol, smp, int(sf["sf_k"]), int(sf["sf_kmax"]), int(sf["sf_whist"]),
-                          float(sf["sf_tau_conv"]), float(sf["sf_tau_high"]), float(sf["sf_var"]))
+                          float(sf["sf_tau_conv"]), float(sf["sf_tau_high"]), float(sf["sf_var"]),
+                          int(lock.get("refresh_budget", 0)),
+                          float(lock.get("refresh_eps", lock["kl_eps"])))
 
 
 # ---- the C ABI under its own names ---------------------------------------------
@@ -315,6 +317,13 @@ class Engine:
 
     def has_prev(self) -> torch.Tensor:
         return self._view(L.DLM_GET_HAS_PREV, torch.int32, (self.run.batch, self.run.seq_len))
+
+    def drift(self) -> torch.Tensor:
+        return self._view(L.DLM_GET_DRIFT, torch.float32, (self.run.batch, self.run.seq_len))
+
+    def refresh_bits(self) -> torch.Tensor:
+        return self._view(L.DLM_GET_REFRESH, torch.int64,
+                          (self.run.batch, (self.run.seq_len + 63) // 64))
 
     def rows(self):
         return (self._view(L.DLM_GET_ROW_SEQ, torch.int32),

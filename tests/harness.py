@@ -10,6 +10,13 @@ the oracle's tokens, lock bits and counters are written over the engine's
 state arrays (tensor copies into the state block, not the ABI override;
 the override path has its own test) and the replay is counted.
 
+With the drift-aware refresh on, the refresh set is compared bit for bit
+every step and the engine's drift against the rule on its own statistics;
+where the engine's float32 drift ranks the locked positions differently from
+the oracle's at the budget boundary, the two drifts there must lie within the
+KL error, and the oracle's drift is written into the engine before the step
+(a "refresh-rank" replay).
+
 ``record`` appends a JSON line per run to the file named by the environment
 variable DLM_PARITY_RECORD (nothing is written when it is unset), so that
 replay counts survive pytest's output capture.
@@ -126,7 +133,7 @@ def _kth_gap(c, k: int) -> float:
 
 
 def explain_difference(shape, run, lock, t, x_before, x_g, x_o, lk_g, lk_o, cnt_g, cnt_o,
-                       seq_o, pos_o, real_o, so, near_tie, dconf, dkl):
+                       seq_o, pos_o, real_o, so, near_tie, dconf, dkl, refresh=None):
     """Asserts that every decision where engine and oracle differ sits inside
     a margin; returns the list of margins used."""
     reasons = set()
@@ -153,6 +160,13 @@ def explain_difference(shape, run, lock, t, x_before, x_g, x_o, lk_g, lk_o, cnt_
     eps, tau = float(lock["kl_eps"]), float(lock["conf_tau"])
     for b, p in diff_lock:
         i = row_of.get((int(b), int(p)))
+        if refresh is not None and refresh[b, p]:
+            # a recomputed locked position: kept or unlocked by its drift
+            assert i is not None and so["has_kl"][i] and \
+                abs(so["kl"][i] - float(lock["refresh_eps"])) < MARGIN, \
+                f"step {t}: refresh decision differs at ({b},{p}) outside margin"
+            reasons.add("refresh-margin")
+            continue
         assert i is not None and real_o[i] and so["has_kl"][i], \
             f"step {t}: lock state differs at ({b},{p}) where no test applies"
         near_kl = abs(so["kl"][i] - eps) < MARGIN
@@ -176,8 +190,32 @@ def run_lockstep(shape, W: Dict, run, lock: Dict, prompts: np.ndarray, steps: Op
     B, N, V = run.batch, run.seq_len, shape.vocab
     reports = []
     T = run.steps if steps is None else steps
+    refresh_on = int(lock.get("refresh_budget", 0)) > 0
     for t in range(T):
         x_before = orc.tokens()
+        pre_reasons = []
+        if refresh_on:
+            # the refresh ranks the locked positions by drift; where the
+            # engine's float32 drift orders them differently from the
+            # oracle's at the budget boundary, the two must be within the
+            # statistics' error there, and the oracle's drift is replayed
+            lk_now = orc.locked()
+            dr_o = orc.drift()
+            dr_g = eng.drift().cpu().numpy()
+            sel_o = oracle.unit_refresh_select(run, lock, lk_now, dr_o)
+            sel_g = oracle.unit_refresh_select(run, lock, lk_now, dr_g)
+            if not np.array_equal(sel_o, sel_g):
+                r = int(lock["refresh_budget"])
+                for b in range(B):
+                    d = np.sort(dr_o[b][lk_now[b] == 1].astype(np.float64))[::-1]
+                    if len(d) > r and sel_o[b].tolist() != sel_g[b].tolist():
+                        tol = (1e-4 + 5e-2 * abs(d[r])) if shape.bf16 else (
+                            2e-6 + 1e-3 * abs(d[r]))
+                        assert np.isfinite(d[r - 1]) and d[r - 1] - d[r] <= 2 * tol, \
+                            f"step {t}: refresh set differs outside the drift error"
+                eng.drift().copy_(torch.from_numpy(dr_o).to(dev))
+                torch.cuda.synchronize()
+                pre_reasons.append("refresh-rank")
         m_gpu = eng.step()
         orc.step()
         torch.cuda.synchronize()
@@ -186,6 +224,10 @@ def run_lockstep(shape, W: Dict, run, lock: Dict, prompts: np.ndarray, steps: Op
         rs, rp, rr = (a.cpu().numpy() for a in eng.rows())
         assert np.array_equal(rs, seq_o) and np.array_equal(rp, pos_o), f"step {t}: active rows"
         assert np.array_equal(rr.astype(np.uint8), real_o), f"step {t}: real flags"
+        rf_o = orc.refresh() if refresh_on else None
+        if refresh_on:
+            rf_g = bits_to_bool(eng.refresh_bits().cpu().numpy().view(np.uint64), N)
+            assert np.array_equal(rf_g, rf_o), f"step {t}: refresh set"
         _, _, flops = eng.last_step_info()
         cf = oracle.closed_form_flops(shape, [orc.m], N)
         assert abs(flops - cf) <= 1e-9 * max(cf, 1.0), f"step {t}: FLOP count {flops} vs {cf}"
@@ -193,6 +235,7 @@ def run_lockstep(shape, W: Dict, run, lock: Dict, prompts: np.ndarray, steps: Op
             orc.lock_update()
             eng.lock_update()
             continue
+        drift_before = eng.drift().cpu().numpy() if refresh_on else None
         _, zo = orc.logits()
         zg = eng.logits().cpu().numpy()[rs, rp]
         fin = np.isfinite(zo)
@@ -248,19 +291,26 @@ def run_lockstep(shape, W: Dict, run, lock: Dict, prompts: np.ndarray, steps: Op
         lock32 = dict(lock, kl_eps=float(np.float32(lock["kl_eps"])),
                       conf_tau=float(np.float32(lock["conf_tau"])))
         assert lock.get("sampler", "semi_ar") == "semi_ar", "SlowFast runs have their own harness"
-        rx, rl, rc = oracle.unit_lock_transition(
+        if refresh_on:
+            lock32["refresh_eps"] = float(np.float32(lock["refresh_eps"]))
+        tr = oracle.unit_lock_transition(
             shape, run, lock32, t, rs, rp, rr.astype(np.uint8), sg["argmax"],
             sg["conf"].astype(np.float64), sg["kl"].astype(np.float64),
-            sg["has_kl"].astype(np.uint8), x_before, locked_before, cnt_before)
+            sg["has_kl"].astype(np.uint8), x_before, locked_before, cnt_before,
+            refresh=rf_o, drift=drift_before)
+        rx, rl, rc = tr[:3]
         assert np.array_equal(rx, x_g), f"step {t}: commit is not the rule on the engine's stats"
         assert np.array_equal(rl, lk_g) and np.array_equal(rc, cnt_g), \
             f"step {t}: lock update is not the rule on the engine's stats"
-        reasons = []
+        if refresh_on:
+            assert np.array_equal(tr[3], eng.drift().cpu().numpy()), \
+                f"step {t}: drift is not the engine's own KL of the step"
+        reasons = list(pre_reasons)
         if not (np.array_equal(x_g, x_o) and np.array_equal(lk_g, lk_o)
                 and np.array_equal(cnt_g, cnt_o)):
-            reasons = explain_difference(shape, run, lock, t, x_before, x_g, x_o, lk_g, lk_o,
-                                         cnt_g, cnt_o, seq_o, pos_o, real_o, so, near_tie,
-                                         dconf, dkl if hk.any() else None)
+            reasons += explain_difference(shape, run, lock, t, x_before, x_g, x_o, lk_g, lk_o,
+                                          cnt_g, cnt_o, seq_o, pos_o, real_o, so, near_tie,
+                                          dconf, dkl if hk.any() else None, refresh=rf_o)
             # every difference lies inside a margin: replay the oracle's decision
             # into the engine's state
             tok_v.copy_(torch.from_numpy(x_o).to(tok_v.device))

@@ -169,3 +169,27 @@ def test_workspace_queries():
     assert L.lib().dlm_op_attention_ws_bytes(1, 20, 1, 1024, 32, 32, 128) > 0
     assert L.lib().dlm_op_attention_ws_bytes(1, 1, 1, 512, 32, 32, 128) == 0
     assert L.lib().dlm_op_attention_ws_bytes(1, 1024, 1, 1024, 32, 32, 128) == 0
+
+
+@pytest.mark.parametrize("field,value", [
+    ("refresh_budget", -1), ("refresh_budget", 513), ("refresh_eps", float("nan")),
+    ("sampler", 1)])
+def test_invalid_refresh_run_rejected(field, value):
+    # the drift-aware refresh needs the semi-AR sampler, 0 <= budget <= seq_len
+    shape, run = synth.CONFIGS["llada8b"]
+    m, r = E.model_desc(shape), E.run_desc(run, synth.LOCK_SETTINGS["refresh"])
+    assert r.refresh_budget == 8 and E.dlm_state_bytes(m, r) > 0
+    setattr(r, field, value)
+    assert E.dlm_state_bytes(m, r) == 0
+
+
+def test_refresh_sequence_limit():
+    # the selection stages a sequence's locked positions in LDS: seq_len <= 4096
+    import dataclasses
+    shape, run = synth.CONFIGS["longctx"]
+    lock = synth.LOCK_SETTINGS["refresh"]
+    assert E.dlm_state_bytes(E.model_desc(shape), E.run_desc(run, lock)) > 0
+    big = dataclasses.replace(run, seq_len=4160)
+    assert E.dlm_state_bytes(E.model_desc(shape), E.run_desc(big, lock)) == 0
+    assert E.dlm_state_bytes(E.model_desc(shape),
+                             E.run_desc(big, dict(lock, refresh_budget=0))) > 0

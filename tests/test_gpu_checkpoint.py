@@ -1,8 +1,9 @@
 """Checkpoint and resume through the C ABI (dlm_checkpoint_save / load): a
 run saved at a step boundary and resumed in a fresh handle, or rewound in the
 same handle, continues bitwise as the uninterrupted run did (tokens, lock
-bits, counters, SlowFast state, per-row statistics, logits and K/V cache at
-every later step), with host and device images; plus the refusals."""
+bits, counters, SlowFast state, drift and refresh set, per-row statistics,
+logits and K/V cache at every later step), with host and device images; plus
+the refusals."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +21,7 @@ CASES = {
     "tiny-fp32-natural": (synth.CONFIGS["tiny"][0], synth.CONFIGS["tiny"][1], "natural", 5),
     "mid-bf16-scheduled": (MID, MID_RUN, "scheduled", 7),
     "mid-bf16-slowfast": (MID, MID_RUN, "slowfast", 9),
+    "mid-bf16-refresh": (MID, MID_RUN, "refresh", 9),
 }
 
 
@@ -30,7 +32,8 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
 
 def _snapshot(eng: E.Engine, with_rows: bool) -> dict:
     s = dict(tokens=eng.tokens(), bits=eng.lock_bits(), counters=eng.counters(),
-             frozen=eng.frozen_bits(), sf=eng.sf_state(), has_prev=eng.has_prev())
+             frozen=eng.frozen_bits(), sf=eng.sf_state(), has_prev=eng.has_prev(),
+             drift=eng.drift(), refresh=eng.refresh_bits())
     kc, vc = eng.kv_cache()
     s.update(kc=kc, vc=vc)
     if with_rows:
