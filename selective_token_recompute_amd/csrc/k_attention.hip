@@ -617,7 +617,11 @@ __global__ __launch_bounds__(64 * QW * KH, 1) void attn32_kernel(
   constexpr int K_INSTR = K_BYTES / 1024, V_INSTR = V_BYTES / 1024;
   constexpr int IPW = (K_INSTR + V_INSTR) / NWV;  // load instructions per wave per tile
   static_assert((K_INSTR + V_INSTR) % NWV == 0, "instructions per wave");
-  static_assert((STAGES - 1) * IPW < 64, "in-flight loads must fit the vmcnt counter");
+  constexpr int QRB = HD * 2, QCH = QRB / 16;  // query vector bytes, 16-byte chunks
+  constexpr int Q_INSTR = QT * QRB / 1024;
+  static_assert(Q_INSTR % NWV == 0, "query load instructions per wave");
+  constexpr int QIPW = Q_INSTR / NWV;
+  static_assert(QIPW + STAGES * IPW < 64, "in-flight loads must fit the vmcnt counter");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -676,12 +680,20 @@ __global__ __launch_bounds__(64 * QW * KH, 1) void attn32_kernel(
       dst[i] = K_BYTES + jv * 1024;
     }
   }
+  // Key tiles in rotated order: query tile bx starts at key tile bx mod
+  // ntiles.  The query tiles of one (sequence, kv head) are consecutive
+  // workgroups of one XCD, so they first request different tiles and the
+  // head's whole K/V is in flight at once, rather than one tile at a time;
+  // each then finds the tiles its siblings fetched in the XCD's L2.  The
+  // online softmax does not depend on the order beyond rounding.
+  const int rot = ntiles > 0 ? bx % ntiles : 0;
   auto issue = [&](int t) {
     unsigned char* st = smem + (t % STAGES) * STAGE;
+    const int kt = t + rot < ntiles ? t + rot : t + rot - ntiles;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int j = wave + i * NWV;
-      const size_t adv = j < K_INSTR ? (size_t)t * KT * HD : (size_t)t * KT;
+      const size_t adv = j < K_INSTR ? (size_t)kt * KT * HD : (size_t)kt * KT;
       attn_dma16(src[i] + adv, st + dst[i]);
     }
   };
@@ -698,31 +710,53 @@ __global__ __launch_bounds__(64 * QW * KH, 1) void attn32_kernel(
       for (int r = 0; r < 16; ++r) oacc[qb][hb][r] = 0.f;
   }
 
+  // The query vectors go to LDS by the same DMA as the tiles, ahead of them:
+  // then every load in flight is of one kind, completes in issue order, and
+  // the wait for the first tile also covers the queries (a register load of
+  // the queries made the compiler wait for every tile in flight before the
+  // first MFMA).  Lane i of instruction j fills slot i % QCH of query vector
+  // j * (64 / QCH) + i / QCH from its chunk slot ^ (vector & (QCH - 1));
+  // vectors past the sequence's last load the tile's first one and are
+  // zeroed in registers.
+  unsigned char* qs = smem + STAGES * STAGE;
 #pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t)
-    if (t < ntiles) issue(t);
-  // query fragments (B operand of S^T) while the first tiles are in flight
-  bf16x8 qf[QB][NKC];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const bf16_t* qp = q + (size_t)row[qb] * nq * HD + (size_t)head[qb] * HD + g * 8;
-#pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      if (qok[qb]) {
-        qf[qb][c] = *(const bf16x8*)(qp + c * 16);
-      } else {
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        qf[qb][c] = *(const bf16x8*)&z;
-      }
-    }
+  for (int i = 0; i < QIPW; ++i) {
+    const int j = wave + i * NWV;
+    const int qi = j * (1024 / QRB) + lane / QCH;
+    const int qv = qbase + qi < Qn ? qbase + qi : qbase;
+    const int lc = (lane % QCH) ^ (qi & (QCH - 1));
+    attn_dma16(q + (size_t)(r0 + qv / G) * nq * HD + (size_t)(gk * G + qv % G) * HD + lc * 8,
+               qs + j * 1024);
   }
+  // every slot of the ring is filled before the loop; from the second tile
+  // on, tile t + STAGES - 1 refills the slot of tile t - 1, which every wave
+  // has finished once it has passed tile t's barrier
+#pragma unroll
+  for (int t = 0; t < STAGES; ++t)
+    if (t < ntiles) issue(t);
+  if (ntiles == 0) attn_wait_vmcnt<0>();  // no DMA may land after the workgroup ends
 
+  bf16x8 qf[QB][NKC];  // query fragments: the B operand of S^T
   const int kofs = kh * KW;  // this wave's first key in a tile
   for (int t = 0; t < ntiles; ++t) {
-    attn_wait_tiles<IPW, STAGES - 1>(min(STAGES - 2, ntiles - 1 - t));
+    if (t == 0) attn_wait_tiles<IPW, STAGES>(min(STAGES - 1, ntiles - 1));
+    else attn_wait_tiles<IPW, STAGES>(min(STAGES - 2, ntiles - 1 - t));
     attn_lds_barrier();
-    if (t + STAGES - 1 < ntiles) issue(t + STAGES - 1);
+    if (t > 0 && t + STAGES - 1 < ntiles) issue(t + STAGES - 1);
     if (!wave_live) continue;  // no valid query in this wave: loads only
+    if (t == 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qi = (qw * QB + qb) * 32 + l32;
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) {
+          const uint4 z = make_uint4(0, 0, 0, 0);
+          const bf16x8 v =
+              *(const bf16x8*)(qs + qi * QRB + (((2 * c + g) ^ (qi & (QCH - 1))) << 4));
+          qf[qb][c] = qok[qb] ? v : *(const bf16x8*)&z;
+        }
+      }
+    }
     const unsigned char* st = smem + (t % STAGES) * STAGE;
     f32x16 s[QB][KB];
 #pragma unroll
@@ -1204,7 +1238,8 @@ template <int HD, int KT, int STAGES, int QW, int KH, int QB, bool SPLIT>
 void launch_a32(dim3 grid, const void* q, const int32_t* row_start, const void* kc,
                 const void* vc, void* o, int N, int nq, int nkv, int kps, int M, float* po,
                 float* pml, hipStream_t s) {
-  constexpr size_t ring = (size_t)STAGES * (KT * HD * 2 + HD * KT * 2);
+  // the ring, then the workgroup's query vectors
+  constexpr size_t ring = (size_t)STAGES * (KT * HD * 2 + HD * KT * 2) + 32 * QW * QB * HD * 2;
   constexpr size_t merge = attn32_merge_bytes<HD, QB>(KH, QW);
   constexpr size_t lds = ring > merge ? ring : merge;
   static_assert(lds <= 160 * 1024, "LDS of a CU");

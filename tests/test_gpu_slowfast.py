@@ -208,7 +208,7 @@ def run_slowfast_lockstep(shape, W, run, lock, prompts):
     orc = oracle.Oracle(shape, W, run, lock, prompts)
     B, N = run.batch, run.seq_len
     rep = dict(steps=0, replays=0, frozen_steps=0, max_frozen=0, returns=0, cycles=0,
-               argmax_near_tie=0, ambiguous=0)
+               argmax_near_tie=0, ambiguous=0, argmax_replays=0)
     returned = np.zeros((B, N), bool)  # unfrozen by the last update
     for t in range(run.steps):
         m = eng.step()
@@ -281,11 +281,23 @@ def run_slowfast_lockstep(shape, W, run, lock, prompts):
             assert np.array_equal(rx, got["tokens"]) and np.array_equal(rf, got["frozen"]) and \
                 np.array_equal(rh, got["has_prev"]) and np.array_equal(rst, got["state"]), \
                 f"step {t}: the engine's decision is not the rule on its own statistics"
-            # (b) the oracle's decision sits within the confidence error of a
+            # (b) a token committed on both sides but different is the
+            # row's argmax at a near tie (asserted for every row above);
+            # every other difference -- the commit set, the frozen set, the
+            # cycle state -- must sit within the confidence error of a
             # comparison the rule made
-            if any(k != "locks" for k in diff):
+            row_of = {(int(b), int(p)): i for i, (b, p) in enumerate(zip(seq_o, pos_o))}
+            x0, xo, xg = pre["x"], want["tokens"].reshape(got["tokens"].shape), got["tokens"]
+            tok_argmax = all(
+                (int(b), int(p)) in row_of and near_tie[row_of[(int(b), int(p))]] and
+                xg[b, p] != x0[b, p] and xo[b, p] != x0[b, p]
+                for b, p in np.argwhere(xg != xo))
+            rest = [k for k in diff if k not in ("locks", "tokens")]
+            if rest or ("tokens" in diff and not tok_argmax):
                 assert ambiguous, \
                     f"step {t}: {diff} differ with decision margin {margin:.3g} > 2 x {dconf:.3g}"
+            elif "tokens" in diff:
+                rep["argmax_replays"] += 1
             for b, p in np.argwhere(got["locks"] != want["locks"]):
                 i = np.nonzero((seq_o == b) & (pos_o == p))[0]
                 assert len(i) == 1 and real_o[i[0]] and so["has_kl"][i[0]], \
@@ -330,7 +342,8 @@ def test_slowfast_lockstep_tiny_fp32(tiny_case):
     print(f"\n[slowfast tiny fp32] end point {e} {rep}")
     append_record(dict(name="slowfast/tiny-fp32", **rep))
     assert rep["frozen_steps"] > 0 and rep["returns"] > 0 and rep["cycles"] > 0
-    assert rep["replays"] <= min(rep["ambiguous"], rep["steps"] // 4), rep
+    assert rep["replays"] - rep["argmax_replays"] <= min(rep["ambiguous"], rep["steps"] // 4), rep
+    assert rep["argmax_replays"] <= rep["steps"] // 16, rep
 
 
 def test_slowfast_lockstep_bf16_two_sequences():
@@ -346,8 +359,10 @@ def test_slowfast_lockstep_bf16_two_sequences():
     # random weights: the masked positions share one input embedding, so
     # their confidences nearly coincide and the ranking the rule takes is
     # within the bf16 confidence error at most steps; a replay happens only
-    # at such an ambiguous step (asserted per step above)
-    assert rep["replays"] <= rep["ambiguous"], rep
+    # at such an ambiguous step (asserted per step above), or where a
+    # committed row's argmax is a near tie
+    assert rep["replays"] - rep["argmax_replays"] <= rep["ambiguous"], rep
+    assert rep["argmax_replays"] <= rep["steps"] // 16, rep
 
 
 @pytest.mark.timeout(1500)
@@ -366,7 +381,8 @@ def test_slowfast_lockstep_depth32():
     append_record(dict(name="slowfast/depth32", **rep))
     assert rep["steps"] == RUN.steps and rep["cycles"] > 0
     assert rep["frozen_steps"] > 0 and rep["returns"] > 0
-    assert rep["replays"] <= rep["ambiguous"], rep
+    assert rep["replays"] - rep["argmax_replays"] <= rep["ambiguous"], rep
+    assert rep["argmax_replays"] <= rep["steps"] // 16, rep
 
 
 def test_slowfast_llada_full_shape_invariants():
