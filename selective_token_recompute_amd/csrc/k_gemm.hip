@@ -553,8 +553,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
         const float* prow = ep.zprev + (size_t)meta[wm * WM + i * 16 + rq + q].slot * N;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int col = n0 + brow(j) + cl;
-          zp[q][j] = col < N ? prow[col] : 0.f;
+          // unconditional (a column past N reads the row's last entry and is
+          // never folded): loads in a branch left the compiler unable to
+          // count them, and it then waited for all of them at every use
+          zp[q][j] = prow[min(n0 + brow(j) + cl, N - 1)];
         }
       }
     };
@@ -572,17 +574,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rl = wm * WM + i * 16 + rq + q;
-        const int row = m0 + rl;
         const RowMeta mt = meta[rl];
         const bool hp = mt.hp != 0;
-        float* zrow = (float*)ep.C + (size_t)mt.slot * N;
         VocabPart a = vpart_empty();
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int col = n0 + brow(j) + cl;
           if (col < N) {
             const float zv = (col == ep.mask_id) ? -INFINITY : acc[i][j][q];
-            if (row < M) zrow[col] = zv;
             vpart_visit<kd>(a, col, zv, cur[q][j], hp, mt.lsep, ep.mask_id);
           }
         }
@@ -606,6 +605,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
       static_for<TM>(rows_fwd);
     else
       static_for<TM>(rows_rev);
+    // The logits are stored only now, after every row block is folded:
+    // loads and stores share the vector-memory counter, so a store issued
+    // between the previous-logit loads made every later wait for a load
+    // also wait for that store to complete (one round trip per row block).
+    // (row blocks expanded at compile time, as above)
+    auto store_rows = [&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rl = wm * WM + i * 16 + rq + q;
+        if (m0 + rl < M) {
+          float* zrow = (float*)ep.C + (size_t)meta[rl].slot * N;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int col = n0 + brow(j) + cl;
+            if (col < N) zrow[col] = (col == ep.mask_id) ? -INFINITY : acc[i][j][q];
+          }
+        }
+      }
+    };
+    static_for<TM>(store_rows);
     __syncthreads();
     for (int t = tid; t < BM; t += 64 * NW) {
       const int row = m0 + t;
