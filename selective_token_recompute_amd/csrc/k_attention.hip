@@ -592,7 +592,7 @@ __device__ __forceinline__ int a32_vswz(int r) {
 
 template <int HD, int QB>
 constexpr size_t attn32_merge_bytes(int KH, int QW) {
-  return KH == 1 ? 0 : (size_t)(KH / 2) * QW * QB * ((HD / 32) * 16 * 64 * 4 + 64 * 8);
+  return KH == 1 ? 0 : (size_t)KH * QW * QB * ((HD / 32) * 16 * 64 * 4 + 64 * 8);
 }
 
 template <int HD, int KT, int STAGES, int QW, int KH, int QB, bool SPLIT>
@@ -827,84 +827,90 @@ __global__ __launch_bounds__(64 * QW * KH, 1) void attn32_kernel(
     }
   }
 
+  // The key groups merge by the log-sum-exp rule in one round: every wave
+  // writes its state to LDS, then wave kh merges head-dim blocks kh, kh + KH,
+  // ... over the KH groups (in group order), normalises and stores them, so
+  // that the merge and the stores are shared by all waves.
+  constexpr int OB = NHB * 16 * 64 * 4;  // O^T registers of one query block
+  constexpr int SB = OB + 64 * 8;        // + (m, l) per lane
+  auto state = [&](int grp, int qb) { return smem + (size_t)((grp * QW + qw) * QB + qb) * SB; };
   if constexpr (KH > 1) {
-    // merge the key groups in pairs by the log-sum-exp rule: in the round of
-    // width h, groups [h, 2h) hand their state to groups [0, h) through LDS;
-    // every wave takes part in every barrier
-    constexpr int OB = NHB * 16 * 64 * 4;          // O^T registers of one query block
-    constexpr int REG = QB * (OB + 64 * 8);       // + (m, l) per lane
-    attn_lds_barrier();  // every wave is done with the tiles in LDS
+    attn_lds_barrier();  // every wave is done with the tiles and queries in LDS
 #pragma unroll
-    for (int h = KH / 2; h >= 1; h /= 2) {
-      if (kh >= h && kh < 2 * h) {
-        unsigned char* mine = smem + ((kh - h) * QW + qw) * REG;
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x4* mine = (f32x4*)state(kh, qb);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+      for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-          for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-              ((f32x4*)(mine + qb * OB))[(hb * 4 + r4) * 64 + lane] =
-                  f32x4{oacc[qb][hb][4 * r4], oacc[qb][hb][4 * r4 + 1], oacc[qb][hb][4 * r4 + 2],
-                        oacc[qb][hb][4 * r4 + 3]};
-          ((float2*)(mine + QB * OB))[qb * 64 + lane] = make_float2(m_run[qb], l_run[qb]);
-        }
-      }
-      attn_lds_barrier();
-      if (kh < h) {
-        const unsigned char* other = smem + (kh * QW + qw) * REG;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float2 ml = ((const float2*)(other + QB * OB))[qb * 64 + lane];
-          const float m = fmaxf(m_run[qb], ml.x);
-          const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m);
-          const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - m);
-#pragma unroll
-          for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const f32x4 v = ((const f32x4*)(other + qb * OB))[(hb * 4 + r4) * 64 + lane];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                oacc[qb][hb][4 * r4 + e] = oacc[qb][hb][4 * r4 + e] * a0 + v[e] * a1;
-            }
-          l_run[qb] = l_run[qb] * a0 + ml.y * a1;
-          m_run[qb] = m;
-        }
-      }
-      attn_lds_barrier();  // the slots are read before the next round writes
+        for (int r4 = 0; r4 < 4; ++r4)
+          mine[(hb * 4 + r4) * 64 + lane] =
+              f32x4{oacc[qb][hb][4 * r4], oacc[qb][hb][4 * r4 + 1], oacc[qb][hb][4 * r4 + 2],
+                    oacc[qb][hb][4 * r4 + 3]};
+      ((float2*)(state(kh, qb) + OB))[lane] = make_float2(m_run[qb], l_run[qb]);
     }
-    if (kh != 0) return;
+    attn_lds_barrier();
   }
 
   // lane l holds query l%32 and head dims 32 hb + 8 i + 4 (l/32) + j in
   // register 4 i + j of block hb
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    float wgt[KH];  // weight of each group's sums
+    float m = m_run[qb], l = l_run[qb];
+    if constexpr (KH > 1) {
+      float mg[KH], lg[KH];
+      m = -INFINITY;
+#pragma unroll
+      for (int kg = 0; kg < KH; ++kg) {
+        const float2 ml = ((const float2*)(state(kg, qb) + OB))[lane];
+        mg[kg] = ml.x;
+        lg[kg] = ml.y;
+        m = fmaxf(m, ml.x);
+      }
+      l = 0.f;
+#pragma unroll
+      for (int kg = 0; kg < KH; ++kg) {
+        wgt[kg] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg[kg] - m);
+        l += lg[kg] * wgt[kg];
+      }
+    }
     if (!qok[qb]) continue;
     const int gq = row[qb] * nq + head[qb];
-    if (SPLIT) {
-      const size_t base = (size_t)bz * M * nq + gq;
+    const size_t base = SPLIT ? (size_t)bz * M * nq + gq : 0;
+    if (SPLIT && kh == 0 && g == 0) *(float2*)(part_ml + base * 2) = make_float2(m, l);
+    const float inv = 1.f / l;
+    bf16_t* op = o + (size_t)row[qb] * nq * HD + (size_t)head[qb] * HD;
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
+    for (int hb = 0; hb < NHB; ++hb) {
+      if (hb % KH != kh) continue;  // wave-uniform
+      f32x16 v;
+      if constexpr (KH > 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *(f32x4*)(part_o + base * HD + hb * 32 + 8 * i + 4 * g) =
-              f32x4{oacc[qb][hb][4 * i], oacc[qb][hb][4 * i + 1], oacc[qb][hb][4 * i + 2],
-                    oacc[qb][hb][4 * i + 3]};
-      if (g == 0) *(float2*)(part_ml + base * 2) = make_float2(m_run[qb], l_run[qb]);
-    } else {
-      const float inv = 1.f / l_run[qb];
-      bf16_t* op = o + (size_t)row[qb] * nq * HD + (size_t)head[qb] * HD;
+        for (int r = 0; r < 16; ++r) v[r] = 0.f;
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
+        for (int kg = 0; kg < KH; ++kg) {
+          const f32x4* st = (const f32x4*)state(kg, qb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint2 w = make_uint2(f2bf2(oacc[qb][hb][4 * i] * inv, oacc[qb][hb][4 * i + 1] * inv),
-                                     f2bf2(oacc[qb][hb][4 * i + 2] * inv,
-                                           oacc[qb][hb][4 * i + 3] * inv));
-          *(uint2*)(op + hb * 32 + 8 * i + 4 * g) = w;
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 x = st[(hb * 4 + r4) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * r4 + e] += wgt[kg] * x[e];
+          }
         }
+      } else {
+        v = oacc[qb][hb];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (SPLIT) {
+          *(f32x4*)(part_o + base * HD + hb * 32 + 8 * i + 4 * g) =
+              f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+        } else {
+          *(uint2*)(op + hb * 32 + 8 * i + 4 * g) =
+              make_uint2(f2bf2(v[4 * i] * inv, v[4 * i + 1] * inv),
+                         f2bf2(v[4 * i + 2] * inv, v[4 * i + 3] * inv));
+        }
+      }
     }
   }
 }
