@@ -268,12 +268,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
     src[i] = base + kbeg + chunk * 8;
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // The gate/up and fused-QKV projections walk their k-slices in an order
+  // rotated by the workgroup's place in the grid, so that the workgroups of
+  // an XCD request different k-offsets of their weight rows at a time (rows
+  // 8 KB apart all share one offset modulo the row size otherwise).  Each
+  // tile's sums then run in a different order, which only rounding sees;
+  // the split-K projections and the LM head keep the plain order (measured
+  // slower there, and the LM head's logits match its unfused form bit for
+  // bit).
+  constexpr bool ROT = !SPLIT && (EPI == kEpiSwiglu || EPI == kEpiQKV);
+  const int krot = ROT && KT > 0 ? lin % KT : 0;
   auto issue = [&](int kt) {
     unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;
+    const int kp = kt + krot < KT ? kt + krot : kt + krot - KT;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int j = wave_u + i * NW;
-      if (EVEN || i < IPW_LO || j < INSTR) dma16(src[i] + kt * BK, st + j * 1024);
+      if (EVEN || i < IPW_LO || j < INSTR) dma16(src[i] + kp * BK, st + j * 1024);
     }
   };
 
