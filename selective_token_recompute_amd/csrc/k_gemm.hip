@@ -268,15 +268,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
     src[i] = base + kbeg + chunk * 8;
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // The gate/up and fused-QKV projections walk their k-slices in an order
-  // rotated by the workgroup's place in the grid, so that the workgroups of
-  // an XCD request different k-offsets of their weight rows at a time (rows
-  // 8 KB apart all share one offset modulo the row size otherwise).  Each
-  // tile's sums then run in a different order, which only rounding sees;
-  // the split-K projections and the LM head keep the plain order (measured
-  // slower there, and the LM head's logits match its unfused form bit for
-  // bit).
-  constexpr bool ROT = !SPLIT && (EPI == kEpiSwiglu || EPI == kEpiQKV);
+  // The gate/up, fused-QKV and LM-head GEMMs walk their k-slices in an
+  // order rotated by the workgroup's place in the grid, so that the
+  // workgroups of an XCD request different k-offsets of their weight rows at
+  // a time (rows 8 KB apart all share one offset modulo the row size
+  // otherwise).  Each tile's sums then run in a different order, which only
+  // rounding sees (and which is the same for the logits and the
+  // logits-with-statistics epilogues of one tile); the split-K projections
+  // keep the plain order (measured slower there).
+  constexpr bool ROT = !SPLIT && (EPI == kEpiSwiglu || EPI == kEpiQKV || EPI == kEpiLogits ||
+                                  EPI == kEpiLogitsStats);
   const int krot = ROT && KT > 0 ? lin % KT : 0;
   auto issue = [&](int kt) {
     unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;

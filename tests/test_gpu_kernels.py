@@ -421,16 +421,18 @@ def test_lm_head_stats_every_tile(cfg):
     _check_lm_head_stats(g, got, zref, ref, ctx, 1001)
 
 
-def test_lm_head_stats_matches_unfused_path():
-    """Same logits and statistics as the LM-head GEMM followed by the separate
-    vocabulary-statistics kernel."""
+@pytest.mark.parametrize("cfg", [1, 12, 13])
+def test_lm_head_stats_matches_unfused_path(cfg):
+    """On one tile configuration, the same logits (bit for bit) and statistics
+    as the LM-head GEMM with the plain logits epilogue followed by the
+    separate vocabulary-statistics kernel."""
     M, V, K = 120, 5000, 256
-    g, got, zref, ref, ctx = _lm_head_stats_case(M, V, K, 0, seed=5)
+    g, got, zref, ref, ctx = _lm_head_stats_case(M, V, K, 0, cfg=cfg, seed=5)
     rs, rp = (torch.from_numpy(ctx[k]).to(DEV) for k in ("rs", "rp"))
     A, W, _ = _gemm_inputs(M, V, K, seed=5 + 11)
     Z = torch.full((2, 96, V), 7.0, device=DEV)
-    ops.gemm(L.DLM_EPI_LOGITS, _dev(A), _dev(W), C=Z, row_seq=rs, row_pos=rp, seq_len=96,
-             mask_id=V - 1)
+    ops.gemm_config(L.DLM_EPI_LOGITS, _dev(A), _dev(W), cfg, splits=1, C=Z, row_seq=rs,
+                    row_pos=rp, seq_len=96, mask_id=V - 1)
     assert np.array_equal(Z.cpu().numpy(), ctx["z"])  # identical logits, bit for bit
     zprev = torch.from_numpy(ctx["zprev"]).to(DEV)
     lse_prev = torch.from_numpy(ctx["lse_prev"]).to(DEV)
@@ -451,8 +453,12 @@ def test_lm_head_stats_ties_and_mask_column():
     mask-token column with the largest logit never counts."""
     M, V, K = 40, 3000, 128
     A, W, _ = _gemm_inputs(M, V, K, seed=77)
+    # integer activations and winner rows 4 e_0: every winner logit is exactly
+    # 4.0 whatever order a tile sums its k-slices in (the other logits stay
+    # well below that: |z| of a few tenths)
+    A = np.random.default_rng(77).integers(-2, 3, size=A.shape).astype(A.dtype)
     A[:, 0] = 1.0
-    row = W[5].copy()
+    row = np.zeros_like(W[5])
     row[0] = 4.0
     W[5] = row      # three equal winners in different column tiles
     W[700] = row
