@@ -268,17 +268,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N,
     src[i] = base + kbeg + chunk * 8;
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // The gate/up, fused-QKV and LM-head GEMMs walk their k-slices in an
-  // order rotated by the workgroup's place in the grid, so that the
-  // workgroups of an XCD request different k-offsets of their weight rows at
-  // a time (rows 8 KB apart all share one offset modulo the row size
-  // otherwise).  Each tile's sums then run in a different order, which only
-  // rounding sees (and which is the same for the logits and the
-  // logits-with-statistics epilogues of one tile); the split-K projections
-  // keep the plain order (measured slower there).
+  // The gate/up, fused-QKV and LM-head GEMMs walk their k-slices in a
+  // rotated order, so that the workgroups of an XCD request different
+  // k-offsets of their weight rows at a time (rows 8 KB apart all share one
+  // offset modulo the row size otherwise): gate/up by the workgroup's place
+  // in the grid, QKV and the LM head by the column tile, which keeps the row
+  // tiles of a weight block in step (four and two of them share it in L2;
+  // each order measured the faster for its class).  Each tile's sums then
+  // run in a different order, which only rounding sees (and which is the
+  // same for the logits and the logits-with-statistics epilogues of one
+  // tile); the split-K projections keep the plain order (measured slower).
   constexpr bool ROT = !SPLIT && (EPI == kEpiSwiglu || EPI == kEpiQKV || EPI == kEpiLogits ||
                                   EPI == kEpiLogitsStats);
-  const int krot = ROT && KT > 0 ? lin % KT : 0;
+  const int krot = !ROT || KT <= 0 ? 0 : (EPI == kEpiSwiglu ? lin : nt) % KT;
   auto issue = [&](int kt) {
     unsigned char* st = smem + (kt % STAGES) * STAGE_BYTES;
     const int kp = kt + krot < KT ? kt + krot : kt + krot - KT;
